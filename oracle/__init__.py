@@ -1,0 +1,8 @@
+"""CPU fp64 oracle for exact softmax attention — test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package. The product path never does.
+"""
+from .attention import attention, attention_head, attention_rows, attention_varlen
+
+__all__ = ["attention", "attention_head", "attention_rows", "attention_varlen"]

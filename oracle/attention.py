@@ -1,0 +1,138 @@
+"""CPU fp64 oracle for exact softmax attention (forward).
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the HIP
+kernels and imports nothing from the product package.
+
+What it computes. The pages state that FlashAttention-2 is exact: it changes
+how attention is executed, not what it computes (chlience notes, "阅读目标与判断
+边界" and §5; paper-graph-ui summary, §3.4 "Algorithm 1 Walkthrough",
+"Mathematical correctness"). So this oracle is the plain, materialised
+definition, written out once per head with no tiling:
+
+    S = scale * Q K^T                          (N x N)
+    S[i, j] = -inf  where causal and j > i
+    m_i = max_j S[i, j]
+    l_i = sum_j exp(S[i, j] - m_i)
+    P = exp(S - m) / l                         (row softmax)
+    O = P V
+    LSE_i = m_i + ln(l_i)
+
+Sources for each line:
+  * S = Q K^T, P = softmax(S), O = P V: chlience notes §1 (研究问题、背景和价值);
+    the 1/sqrt(d) scale inside the score: llm-infra-atlas "FlashAttention" §1
+    (为什么 attention 是 memory-bound). The scale is a parameter here.
+  * the two-pass safe softmax (row max, sum of exp(S - m), divide):
+    paper-graph-ui summary §3.4, "FlashAttention's Online Softmax", the
+    standard (non-online) three-step approach.
+  * LSE = m + log(l), natural log: chlience notes §5.2 (算法语义层);
+    paper-graph-ui §3.4, "Tweak 2: Store Logsumexp".
+  * causal: entries with column index greater than row index are -inf:
+    paper-graph-ui §3.4, "Causal masking optimization"; chlience notes §5.6.
+
+Readings where the pages are silent (each listed in the design doc):
+  * the scale multiplies Q K^T before the softmax, and LSE is taken over the
+    scaled scores, in natural log;
+  * the scale is the float32 value the kernel receives, widened to fp64;
+  * a row with no allowed key (cannot happen for square causal or
+    non-causal attention) would give O = 0 and LSE = -inf.
+
+Every function here is pinned by tests/test_oracle_pins.py (brute force,
+closed forms, library routines, invariants and the pages' online
+recurrence); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["attention", "attention_head", "attention_rows", "attention_varlen"]
+
+
+def _as_f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _softmax_rows(s: np.ndarray):
+    """Two-pass safe softmax of each row of s (entries may be -inf).
+
+    Returns (P, LSE). Rows whose entries are all -inf give P = 0, LSE = -inf.
+    """
+    m = s.max(axis=1, keepdims=True)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe)                # exp(-inf) = 0 for masked entries
+    l = e.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(l > 0.0, e / np.where(l > 0.0, l, 1.0), 0.0)
+        lse = np.where(l[:, 0] > 0.0, m_safe[:, 0] + np.log(np.where(l[:, 0] > 0.0, l[:, 0], 1.0)),
+                       -np.inf)
+    return p, lse
+
+
+def attention_head(q, k, v, causal: bool, scale: float):
+    """Exact attention for one head.
+
+    q, k, v: [N, d] arrays (converted to float64). Returns (O [N, d],
+    LSE [N]) in float64.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    n = q.shape[0]
+    if n == 0:
+        return np.zeros((0, v.shape[1])), np.zeros((0,))
+    s = float(scale) * (q @ k.T)
+    if causal:
+        s[np.triu_indices(n, k=1)] = -np.inf     # key index j > query index i
+    p, lse = _softmax_rows(s)
+    return p @ v, lse
+
+
+def attention(q, k, v, causal: bool, scale: float):
+    """Exact attention over [B, H, N, d] inputs; returns (O [B,H,N,d], LSE [B,H,N])."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, _ = q.shape
+    o = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], causal, scale)
+    return o, lse
+
+
+def attention_rows(q, k, v, causal: bool, scale: float, rows):
+    """Exact attention for selected query rows of one head.
+
+    The softmax is per row, so row i of the result needs only q_i and all of
+    K and V; this evaluates the same definition as ``attention_head`` on a
+    subset of rows (used to check very large problems one row at a time).
+    q, k, v: [N, d]. rows: integer indices into [0, N). Returns
+    (O [len(rows), d], LSE [len(rows)]).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    n = k.shape[0]
+    s = float(scale) * (q[rows] @ k.T)
+    if causal:
+        s[np.arange(n)[None, :] > rows[:, None]] = -np.inf
+    p, lse = _softmax_rows(s)
+    return p @ v, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
+    """Exact attention over a packed batch of sequences.
+
+    q, k, v: [H, T, d]; cu_seqlens: [S + 1] offsets with cu[0] = 0 and
+    cu[S] = T. Sequence s occupies tokens [cu[s], cu[s+1]) of every head and
+    attends only within itself; the causal mask uses indices local to the
+    sequence. Returns (O [H, T, d], LSE [H, T]).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    H, T, _ = q.shape
+    o = np.zeros(q.shape[:2] + (v.shape[2],))
+    lse = np.zeros((H, T))
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        for h in range(H):
+            o[h, a:b], lse[h, a:b] = attention_head(q[h, a:b], k[h, a:b], v[h, a:b], causal, scale)
+    return o, lse
