@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark: exact softmax attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+One step = one forward over the whole batch of the workload (all of the hot path runs in
+one kernel launch). The default workload is the long-context causal one, B=1 H=16 N=16384
+d=128, the configuration the FLOP-rate target is stated on. Inputs are generated once,
+copied to HBM, and stay resident; the timed region covers K launches bracketed by
+synchronisations, timed with HIP events recorded on the stream the kernels are launched on
+(torch's current stream, which the binding passes to the C ABI).
+
+Metric: attention forward TFLOP/s with FLOPs = 4*B*H*N^2*d, halved for causal (the paper's
+accounting; paper-graph-ui summary, "5. Experimental Analysis", Metrics), and the fraction
+of MI355X's dense bf16 MFMA peak.
+
+Prints ONE JSON line. ``roofline.traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE
+counter runs ingested with ``--ingest-counters`` (stored under profiles/ together with the
+hash of the kernel source they were taken on); it is null when the source has changed
+since. ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PF)
+PEAK_HBM_GBS = 8000.0
+A100_FIG5D_16K_TFLOPS = 197.0   # the pages' FA2 forward, causal, d=128, 16k (A100; context only)
+KERNEL_SRC = os.path.join(ROOT, "exact_softmax_attention_amd", "csrc", "fa2_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_c4_traffic.json")
+COPY_BYTES = 1 << 30   # the calibration copy kernel moves 1 GiB in and 1 GiB out
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w, lengths=None) -> int:
+    """Q, K, V read once and O written once (bf16), LSE written once (fp32)."""
+    if w.varlen:
+        T = sum(lengths)
+        return 8 * w.H * T * w.d + 4 * w.H * T
+    return 8 * w.B * w.H * w.N * w.d + 4 * w.B * w.H * w.N
+
+
+def load_traffic():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t
+
+
+def cpu_baseline(w, q, k, v, heads: int):
+    """Time the fp64 oracle on `heads` heads of batch 0 (all rows)."""
+    import numpy as np
+    from oracle import attention_head
+    from synthetic import metric_flops
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    for h in range(heads):
+        attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
+                       w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    f = metric_flops(1, heads, w.N, w.d, w.causal)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, all {w.N} rows, fp64 numpy "
+                      f"({dt:.2f} s; BLAS threads = cores)",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def run(args):
+    import torch
+
+    import exact_softmax_attention_amd as fa2
+    from synthetic import WORKLOADS, metric_flops, varlen_metric_flops, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    lengths = None
+    if w.varlen:
+        q, k, v, cu, lengths = workload_inputs(w)
+        qd, kd, vd, cud = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:2], dtype=torch.float32, device=dev)
+        maxlen = max(lengths)
+        flops = varlen_metric_flops(lengths, w.H, w.d, w.causal)
+
+        def step():
+            fa2.fwd_varlen(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                           variant=args.variant)
+    else:
+        q, k, v = workload_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        flops = metric_flops(w.B, w.H, w.N, w.d, w.causal)
+
+        def step():
+            fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, variant=args.variant)
+
+    if args.calib_copy:   # a plain copy kernel of known size, for counter calibration
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    traffic = None
+    t = load_traffic()
+    if t is not None:
+        traffic = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+
+    variant = fa2.variant_name(w.d, args.variant)
+    config = {"workload": f"{w.name}: {w.description}", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+              "causal": w.causal, "kernel_variant": variant}
+    if w.varlen:
+        config.update({"lengths": lengths, "total_tokens": sum(lengths)})
+    out = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3) if w.name == "c4" else None),
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": algorithmic_bytes(w, lengths),
+            "flops_per_launch": flops,
+            "kernel_ms": round(ms, 5),
+        },
+    }
+    if args.cpu_baseline_heads > 0:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_baseline_heads) if not w.varlen else None
+    print(json.dumps(out), flush=True)
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, steps: int):
+    """Turn two rocprofv3 --pmc counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) into the
+    per-launch HBM traffic of the attention kernel, scaled by the calibration copy kernel."""
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    out = {"kernel_source_sha256": kernel_source_hash()}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        attn = [v for n, vs in vals.items() if "fa2_fwd_kernel" in n for v in vs]
+        copy = [v for n, vs in vals.items() if "fa2_fwd_kernel" not in n and max(vs) > COPY_BYTES / 1024 * 0.5
+                for v in vs]
+        if not attn or not copy:
+            raise SystemExit(f"{path}: need both the attention kernel and the calibration copy")
+        factor = (COPY_BYTES / 1024) / max(copy)          # counter reads KiB
+        per_launch = sorted(attn)[len(attn) // 2] * 1024 * factor
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        out[f"{key}_bytes_per_launch"] = per_launch
+        out[f"{key}_copy_factor"] = factor
+        out[f"{key}_raw_kib_median"] = sorted(attn)[len(attn) // 2]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--cpu-baseline-heads", type=int, default=1,
+                    help="(batch, head) pairs of the workload the CPU oracle is timed on (0: skip)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB copy kernel (counter calibration for --ingest-counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, steps=args.steps)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards across GPUs by (batch, head) with no communication; only the "
+              "one-GPU share is built).", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+"""ctypes marshalling for libfa2.so (see include/fa2.h for the C ABI)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+FA2_ABI_VERSION = 1
+
+STATUS = {
+    0: "FA2_OK",
+    1: "FA2_ERR_NULL_PTR",
+    2: "FA2_ERR_BAD_SHAPE",
+    3: "FA2_ERR_UNSUPPORTED_HEADDIM",
+    4: "FA2_ERR_MISALIGNED",
+    5: "FA2_ERR_BAD_SCALE",
+    6: "FA2_ERR_NO_DEVICE",
+    7: "FA2_ERR_LAUNCH",
+    8: "FA2_ERR_BAD_VARIANT",
+    9: "FA2_ERR_TOO_LARGE",
+}
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_float = ctypes.c_float
+
+_SIGNATURES = {
+    "fa2_fwd": ([_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_void_p], _c_int),
+    "fa2_fwd_variant": ([_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_int, _c_void_p], _c_int),
+    "fa2_fwd_varlen": ([_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
+    "fa2_fwd_varlen_variant": ([_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_int, _c_void_p], _c_int),
+    "fa2_num_variants": ([_c_int], _c_int),
+    "fa2_fwd_geometry": ([_c_int] * 6 + [ctypes.POINTER(_c_int)] * 4, _c_int),
+    "fa2_status_str": ([_c_int], ctypes.c_char_p),
+    "fa2_variant_name": ([_c_int, _c_int], ctypes.c_char_p),
+    "fa2_abi_version": ([], _c_int),
+}
+
+_LIB = None
+
+
+class Fa2Error(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(PKG_DIR, "libfa2.so")
+
+
+def load_library():
+    """Load libfa2.so (built in-tree). Raises loudly if it is missing: there is no fallback."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run `python -m exact_softmax_attention_amd.build` "
+                              "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(path)
+        for name, (argtypes, restype) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = argtypes
+            fn.restype = restype
+        if lib.fa2_abi_version() != FA2_ABI_VERSION:
+            raise ImportError(f"libfa2.so ABI {lib.fa2_abi_version()} != binding ABI {FA2_ABI_VERSION}")
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int):
+    if status != 0:
+        raise Fa2Error(status, load_library().fa2_status_str(status).decode())
+
+
+def num_variants(d: int) -> int:
+    return load_library().fa2_num_variants(d)
+
+
+def variant_name(d: int, variant: int) -> str:
+    return load_library().fa2_variant_name(d, variant).decode()
+
+
+def geometry(B: int, H: int, N: int, d: int, causal: bool = False, variant: int = 0) -> dict:
+    """Launch geometry computed on the host (no GPU needed)."""
+    out = [_c_int(0) for _ in range(4)]
+    _check(load_library().fa2_fwd_geometry(B, H, N, d, int(causal), variant, *[ctypes.byref(x) for x in out]))
+    return {"num_workgroups": out[0].value, "block_rows": out[1].value,
+            "block_cols": out[2].value, "lds_bytes": out[3].value}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(dev) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check_tensor(name, t, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU (HIP) tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, variant: int = 0):
+    """O, LSE = softmax(scale * q k^T [causal mask]) v for bf16 [B, H, N, d] tensors.
+
+    Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N]); ``out``/``lse`` may be given
+    preallocated. Enqueued on torch's current stream of q's device.
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor("out", out, torch.bfloat16, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    if out.shape != q.shape or tuple(lse.shape) != (B, H, N) or out.device != q.device or lse.device != q.device:
+        raise ValueError("out/lse shape or device mismatch")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 B, H, N, d, int(bool(causal)), float(scale), int(variant), _stream_ptr(q.device))
+    _check(st)
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
+               out=None, lse=None, variant: int = 0):
+    """Packed variable-length forward over bf16 [H, T, d] tensors.
+
+    ``cu_seqlens`` is an int32 GPU tensor [num_seqs + 1]; sequence s owns tokens
+    [cu[s], cu[s+1]). Returns (o bf16 [H, T, d], lse fp32 [H, T]).
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, 3)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ")
+    H, T, d = q.shape
+    num_seqs = cu_seqlens.numel() - 1
+    if num_seqs < 0:
+        raise ValueError("cu_seqlens must have at least one entry")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_tensor("out", out, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    if out.shape != q.shape or tuple(lse.shape) != (H, T):
+        raise ValueError("out/lse shape mismatch")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_fwd_varlen_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                        cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, d,
+                                        int(bool(causal)), float(scale), int(variant), _stream_ptr(q.device))
+    _check(st)
+    return out, lse

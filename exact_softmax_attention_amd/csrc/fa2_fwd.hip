@@ -1,0 +1,577 @@
+// fa2_fwd.hip — gfx950 (CDNA4) forward kernels for exact softmax attention, and the C ABI
+// declared in include/fa2.h.
+//
+// Page abbreviations used below:
+//   [CHL] "FlashAttention 2: Faster Attention with Better Parallelism and Work Partitioning",
+//         reading notes at papers.chlience.com
+//   [LAN] "Flash Attention 2 (FA2)", languisher.top
+//   [ATL] "FlashAttention", llm-infra-atlas
+//   [PGU] "FlashAttention-2: Faster Attention with Better Parallelism and Work Partitioning",
+//         paper-graph-ui summary
+//
+// One workgroup owns one block of BR = 32*WAVES query rows of one (batch, head) or
+// (sequence, head) pair, and walks the key/value tiles of BC keys in order ([CHL] 5.1, 5.4:
+// query row blocks are the outer, parallel loop; key/value blocks the inner, sequential
+// one). Each 64-lane wave owns 32 whole query rows, so no statistic is ever shared between
+// waves ([CHL] 5.5 split-Q; [PGU] 3.4 "warp-level work partitioning"). Per tile and wave:
+//
+//   S^T  = K_j Q_i^T          bf16 MFMA 32x32x16, fp32 accumulate      (a4)
+//   mask                      only on diagonal / ragged tiles            (a5)
+//   m'   = max(m, rowmax S·c); P~ = exp2(S·c - m'); l = 2^(m-m') l + rowsum P~   (a6)
+//   O~^T = 2^(m-m') O~^T + V_j^T P~^T   bf16 MFMA, fp32 accumulate      (a7)
+//
+// and after the last tile O = O~ / l, LSE = (m + log2 l)·ln2 ([CHL] 5.2; [PGU] 3.4
+// "Algorithm 1 Walkthrough"; the rescale multiplies by 2^(m-m') <= 1 as in the erratum of
+// [LAN] "减少非矩阵乘法运算"). c = scale·log2(e) folds the softmax scale into the base-2
+// exponential the hardware provides (v_exp_f32 computes 2^x); [ATL] 2 notes the upstream
+// rescale also uses exp2.
+//
+// Why S^T and not S: a 32x32 MFMA result gives each lane one column and 16 rows. Computing
+// S^T = K Q^T puts one query per lane column, so a lane holds 16 keys of a single query per
+// 32-key block: the row max and row sum are in-lane, plus one exchange between the two
+// 32-lane halves. The same lane layout is exactly the B operand the PV product needs
+// (O^T = V^T P^T, one query per lane column, 8 consecutive contraction positions per lane),
+// so P~ never leaves registers. The contraction positions of that B operand map to keys
+// through the fixed permutation kappa below; V^T is stored in LDS in that permuted key order
+// so that its A-operand fragment is one contiguous 16-byte LDS read.
+//
+// MFMA lane layouts used (v_mfma_f32_32x32x16_bf16, wave64, lane l, element e):
+//   A[m][k]: m = l % 32, k = 8*(l / 32) + e          (8 bf16 per lane)
+//   B[k][n]: n = l % 32, k = 8*(l / 32) + e          (8 bf16 per lane)
+//   C[m][n]: n = l % 32, m = 8*(r / 4) + 4*(l / 32) + r % 4, r = 0..15   (16 fp32 per lane)
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa2.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Kernel arguments (passed by value).
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int* cu_seqlens;  // varlen only
+  int nb;                 // batch size, or number of sequences (varlen)
+  int H;
+  int N;                  // sequence length, or max_seqlen (varlen)
+  int T;                  // tokens per head plane: N, or total_tokens (varlen)
+  int tr;                 // row blocks per (batch|sequence, head)
+  int heads_per_xcd;      // > 0: XCD-aware workgroup order (nb*H divisible by 8)
+  float c;                // |scale| * log2(e)
+  uint32_t qflip;         // 0x80008000 negates Q (scale < 0), else 0
+};
+
+// Compile-time tile geometry.
+template <int D, int BC>
+struct Tile {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BR = 32 * WAVES;        // query rows per workgroup
+  static constexpr int KSTRIDE = D + 8;        // K row pitch in LDS (bf16), +16 B breaks bank aliasing
+  static constexpr int VSTRIDE = BC + 8;       // V^T row pitch in LDS (bf16)
+  static constexpr int KTILE = BC * KSTRIDE;   // bf16 per K stage
+  static constexpr int VTILE = D * VSTRIDE;    // bf16 per V^T stage
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;   // two stages (double buffer)
+  static constexpr int NKB = BC / 32;          // 32-key blocks per tile
+  static constexpr int NKC = D / 16;           // 16-wide contraction steps of QK^T
+  static constexpr int NDB = D / 32;           // 32-wide d blocks of O^T
+  static constexpr int NPC = BC / 16;          // 16-key contraction steps of PV
+  static constexpr int KLOADS = BC * D / 8 / THREADS;    // 16-B K loads per thread and tile
+  static constexpr int VUNITS = BC * D / 32 / THREADS;   // (4 keys x 8 d) V units per thread
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(KLOADS >= 1 && KLOADS * 8 * THREADS == BC * D, "K staging must tile exactly");
+  static_assert(VUNITS >= 1 && VUNITS * 32 * THREADS == BC * D, "V staging must tile exactly");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Position of key offset o (0..15) inside a 16-key group of V^T in LDS. It is the order in
+// which the S^T accumulator lanes present keys as PV contraction positions: offsets 4..7
+// and 8..11 trade places (an involution).
+__device__ __forceinline__ int kappa4(int o) {
+  const int g = o >> 2;                              // 4-key group 0..3
+  const int gs = ((g & 1) << 1) | ((g >> 1) & 1);    // swap groups 1 and 2
+  return (gs << 2) | (o & 3);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 t = {(__bf16)lo, (__bf16)hi};               // round-to-nearest-even
+  return __builtin_bit_cast(uint32_t, t);
+}
+
+// Workgroup id -> (batch|sequence * H + head, row block). With the XCD-aware order,
+// workgroup id goes to XCD id % 8 (round-robin dispatch), and each XCD is given a
+// contiguous set of heads so the K/V of a head stay in one XCD's L2. Causal launches visit
+// row blocks heaviest first (largest i has the most key tiles).
+template <bool CAUSAL>
+__device__ __forceinline__ void decode_block(const Params& p, int& bh, int& i) {
+  const int id = blockIdx.x;
+  if (p.heads_per_xcd > 0) {
+    const int x = id & 7, slot = id >> 3, hpx = p.heads_per_xcd;
+    int hl;
+    if (CAUSAL) {
+      i = p.tr - 1 - slot / hpx;
+      hl = slot - (slot / hpx) * hpx;
+    } else {
+      hl = slot / p.tr;
+      i = slot - hl * p.tr;
+    }
+    bh = x * hpx + hl;
+  } else {
+    const int nbh = p.nb * p.H;
+    i = p.tr - 1 - id / nbh;
+    bh = id - (id / nbh) * nbh;
+  }
+}
+
+template <int D, int BC, bool CAUSAL, bool VARLEN>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void fa2_fwd_kernel(Params p) {
+  using TL = Tile<D, BC>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TL::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;   // MFMA column (query) / A-row index
+  const int hl = lane >> 5;    // which 32-lane half
+
+  // ---- a1: work decode ----------------------------------------------------------------
+  int bh, i;
+  decode_block<CAUSAL>(p, bh, i);
+  const int bi = bh / p.H;
+  const int h = bh - bi * p.H;
+  int seq_len;
+  size_t row0;  // index of this sequence's first token in the [.., T, D] arrays
+  if (VARLEN) {
+    int a = p.cu_seqlens[bi];
+    int e = p.cu_seqlens[bi + 1];
+    a = min(max(a, 0), p.T);
+    e = min(max(e, a), p.T);
+    seq_len = e - a;
+    row0 = (size_t)h * (size_t)p.T + (size_t)a;
+  } else {
+    seq_len = p.N;
+    row0 = (size_t)bh * (size_t)p.N;
+  }
+  const int q0 = i * TL::BR;
+  if (q0 >= seq_len) return;  // uniform over the workgroup (varlen rows past the end)
+
+  const uint16_t* __restrict__ qh = p.q + row0 * D;
+  const uint16_t* __restrict__ kh = p.k + row0 * D;
+  const uint16_t* __restrict__ vh = p.v + row0 * D;
+
+  // Key tiles to visit: causal stops after the tile holding this block's last query.
+  const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
+  const int nt = (kv_end + BC - 1) / BC;
+
+  // ---- a2: this wave's 32 query rows as MFMA B fragments (Q^T), once -----------------
+  const int qw0 = q0 + wave * 32;           // first query row of this wave
+  const int qrow = qw0 + l32;               // the query this lane's column holds
+  bf16x8 qf[TL::NKC];
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+    if (qrow < seq_len) t = *(const u32x4*)(qh + (size_t)qrow * D + kc * 16 + hl * 8);
+    t ^= p.qflip;
+    qf[kc] = as_bf16x8(t);
+  }
+
+  // ---- running state (fp32, registers) -----------------------------------------------
+  f32x16 oacc[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) oacc[db] = (f32x16){};
+  float m_run = -INFINITY;  // running max of S·c (base-2 domain)
+  float l_run = 0.f;        // this lane's partial running sum (its half of the keys)
+
+  // ---- a3: K/V staging (global -> registers -> LDS, double buffered) ------------------
+  u32x4 kreg[TL::KLOADS];
+  u32x4 vreg[TL::VUNITS][4];
+
+  auto load_tile = [&](int j) {
+    const int kbase = j * BC;
+#pragma unroll
+    for (int r = 0; r < TL::KLOADS; ++r) {
+      const int id = r * TL::THREADS + tid;
+      const int row = id / (D / 8), ch = id % (D / 8);
+      const int key = kbase + row;
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (key < seq_len) t = *(const u32x4*)(kh + (size_t)key * D + ch * 8);
+      kreg[r] = t;
+    }
+#pragma unroll
+    for (int u = 0; u < TL::VUNITS; ++u) {
+      const int id = u * TL::THREADS + tid;
+      const int g4 = id % (BC / 4), dc = id / (BC / 4);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = kbase + 4 * g4 + rr;
+        u32x4 t = {0u, 0u, 0u, 0u};   // keys past the end are zero so 0 * V stays finite
+        if (key < seq_len) t = *(const u32x4*)(vh + (size_t)key * D + dc * 8);
+        vreg[u][rr] = t;
+      }
+    }
+  };
+
+  auto store_tile = [&](int stage) {
+    uint16_t* ks = smem + stage * TL::STAGE;
+    uint16_t* vs = ks + TL::KTILE;
+#pragma unroll
+    for (int r = 0; r < TL::KLOADS; ++r) {
+      const int id = r * TL::THREADS + tid;
+      const int row = id / (D / 8), ch = id % (D / 8);
+      *(u32x4*)(ks + row * TL::KSTRIDE + ch * 8) = kreg[r];
+    }
+#pragma unroll
+    for (int u = 0; u < TL::VUNITS; ++u) {
+      const int id = u * TL::THREADS + tid;
+      const int g4 = id % (BC / 4), dc = id / (BC / 4);
+      const int key0 = 4 * g4;
+      const int pos0 = (key0 & ~15) | kappa4(key0 & 15);
+      // 4 keys x 8 d held as 4 rows of 4 dwords (2 d each) -> 8 d rows of 4 keys.
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t r0 = vreg[u][0][w], r1 = vreg[u][1][w];
+        const uint32_t r2 = vreg[u][2][w], r3 = vreg[u][3][w];
+        u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
+        u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
+        *(u32x2*)(vs + (dc * 8 + 2 * w) * TL::VSTRIDE + pos0) = lo;
+        *(u32x2*)(vs + (dc * 8 + 2 * w + 1) * TL::VSTRIDE + pos0) = hi;
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < nt; ++j) {
+    if (j + 1 < nt) load_tile(j + 1);   // in flight while tile j is computed
+
+    const int key0 = j * BC;
+    const uint16_t* ks = smem + (j & 1) * TL::STAGE;
+    const uint16_t* vs = ks + TL::KTILE;
+    // a5: a wave whose rows all precede this tile's first key, or whose rows are all past
+    // the end of the sequence, has nothing to add here (it still joins the barrier).
+    const bool active = (!CAUSAL || key0 <= qw0 + 31) && (qw0 < seq_len);
+    if (active) {
+      // ---- a4: S^T = K_j Q^T --------------------------------------------------------
+      f32x16 s[TL::NKB];
+#pragma unroll
+      for (int kb = 0; kb < TL::NKB; ++kb) {
+        s[kb] = (f32x16){};
+#pragma unroll
+        for (int kc = 0; kc < TL::NKC; ++kc) {
+          const bf16x8 a = *(const bf16x8*)(ks + (kb * 32 + l32) * TL::KSTRIDE + kc * 16 + hl * 8);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+        }
+      }
+
+      // ---- a5: mask on diagonal and ragged tiles only ---------------------------------
+      const bool need_mask = (CAUSAL && key0 + BC - 1 > qw0) || (key0 + BC > seq_len);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool dead = (CAUSAL && key > qrow) || key >= seq_len;
+            if (dead) s[kb][r] = -INFINITY;
+          }
+      }
+
+      // ---- a6: online softmax (fp32) ------------------------------------------------
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));            // the other 16 keys of each 32
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * p.c;
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 on the first tile
+      const bool grew = m_new > m_run;
+      m_run = m_new;
+      l_run *= alpha;
+      // Skip the O~ rescale when no row of the wave changed its max (alpha == 1 exactly).
+      if (__any(grew)) {
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c, -m_use));
+          if (need_mask) e = (s[kb][r] == -INFINITY) ? 0.f : e;
+          s[kb][r] = e;
+          rs += e;
+        }
+      l_run += rs;
+
+      // ---- a7: O~^T += V_j^T P~^T ---------------------------------------------------
+#pragma unroll
+      for (int c = 0; c < TL::NPC; ++c) {
+        const f32x16& sb = s[c >> 1];
+        const int r0 = (c & 1) * 8;
+        u32x4 pw = {pack_bf16x2(sb[r0 + 0], sb[r0 + 1]), pack_bf16x2(sb[r0 + 2], sb[r0 + 3]),
+                    pack_bf16x2(sb[r0 + 4], sb[r0 + 5]), pack_bf16x2(sb[r0 + 6], sb[r0 + 7])};
+        const bf16x8 pf = as_bf16x8(pw);
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db) {
+          const bf16x8 a = *(const bf16x8*)(vs + (db * 32 + l32) * TL::VSTRIDE + c * 16 + hl * 8);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (j + 1 < nt) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- a8: epilogue: O = O~ / l, LSE = (m + log2 l) ln 2 --------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow < seq_len) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = p.o + (row0 + (size_t)qrow) * D;
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
+                   pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+        *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
+      }
+    if (hl == 0) {
+      p.lse[row0 + (size_t)qrow] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// ---- host side ------------------------------------------------------------------------
+
+typedef const void* KernelFn;
+
+struct Variant {
+  const char* name;
+  int d;
+  int br;
+  int bc;
+  int lds;
+  KernelFn fixed[2];   // [causal]
+  KernelFn varlen[2];  // [causal]
+};
+
+template <int D, int BC>
+Variant make_variant(const char* name) {
+  using TL = Tile<D, BC>;
+  Variant v;
+  v.name = name;
+  v.d = D;
+  v.br = TL::BR;
+  v.bc = BC;
+  v.lds = TL::LDS_BYTES;
+  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false>;
+  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false>;
+  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true>;
+  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true>;
+  return v;
+}
+
+const Variant* variants_for(int d, int* count) {
+  static const Variant v64[] = {make_variant<64, 128>("d64_br128_bc128")};
+  static const Variant v128[] = {make_variant<128, 64>("d128_br128_bc64")};
+  if (d == 64) {
+    *count = (int)(sizeof(v64) / sizeof(v64[0]));
+    return v64;
+  }
+  if (d == 128) {
+    *count = (int)(sizeof(v128) / sizeof(v128[0]));
+    return v128;
+  }
+  *count = 0;
+  return nullptr;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 int d, float scale, int variant, const Variant** out) {
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL_PTR;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA2_ERR_MISALIGNED;
+  if (!isfinite(scale)) return FA2_ERR_BAD_SCALE;
+  int count = 0;
+  const Variant* vs = variants_for(d, &count);
+  if (variant < 0 || variant >= count) return FA2_ERR_BAD_VARIANT;
+  *out = &vs[variant];
+  return FA2_OK;
+}
+
+int launch(const Variant& var, bool varlen, bool causal, Params& p, int num_wg, void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
+  KernelFn fn = varlen ? var.varlen[causal ? 1 : 0] : var.fixed[causal ? 1 : 0];
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)num_wg), dim3(256), args, 0,
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+void fill_scale(Params& p, float scale) {
+  p.c = fabsf(scale) * kLog2e;
+  p.qflip = scale < 0.f ? 0x80008000u : 0u;
+}
+
+int heads_per_xcd(long long nbh) { return (nbh % 8 == 0) ? (int)(nbh / 8) : 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa2_abi_version(void) { return FA2_ABI_VERSION; }
+
+int fa2_num_variants(int d) {
+  int count = 0;
+  variants_for(d, &count);
+  return count;
+}
+
+const char* fa2_variant_name(int d, int variant) {
+  int count = 0;
+  const Variant* vs = variants_for(d, &count);
+  if (variant < 0 || variant >= count) return "";
+  return vs[variant].name;
+}
+
+const char* fa2_status_str(int status) {
+  switch (status) {
+    case FA2_OK: return "ok";
+    case FA2_ERR_NULL_PTR: return "a required pointer is NULL";
+    case FA2_ERR_BAD_SHAPE: return "bad shape (B, H must be > 0, N >= 0; varlen sizes consistent)";
+    case FA2_ERR_UNSUPPORTED_HEADDIM: return "unsupported head dimension (64 or 128)";
+    case FA2_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 B, lse 4 B)";
+    case FA2_ERR_BAD_SCALE: return "scale is not finite";
+    case FA2_ERR_NO_DEVICE: return "no usable HIP device";
+    case FA2_ERR_LAUNCH: return "kernel launch failed";
+    case FA2_ERR_BAD_VARIANT: return "kernel variant out of range";
+    case FA2_ERR_TOO_LARGE: return "problem too large (grid or index overflow)";
+    default: return "unknown status";
+  }
+}
+
+int fa2_fwd_geometry(int B, int H, int N, int d, int causal, int variant, int* num_workgroups,
+                     int* block_rows, int* block_cols, int* lds_bytes) {
+  (void)causal;
+  if (B <= 0 || H <= 0 || N < 0) return FA2_ERR_BAD_SHAPE;
+  int count = 0;
+  const Variant* vs = variants_for(d, &count);
+  if (!vs) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (variant < 0 || variant >= count) return FA2_ERR_BAD_VARIANT;
+  const Variant& var = vs[variant];
+  const long long tr = ((long long)N + var.br - 1) / var.br;
+  const long long wg = tr * (long long)B * (long long)H;
+  if (wg > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  if (num_workgroups) *num_workgroups = (int)wg;
+  if (block_rows) *block_rows = var.br;
+  if (block_cols) *block_cols = var.bc;
+  if (lds_bytes) *lds_bytes = var.lds;
+  return FA2_OK;
+}
+
+int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int d, int causal, float scale, int variant, void* stream) {
+  if (B <= 0 || H <= 0 || N < 0) return FA2_ERR_BAD_SHAPE;
+  if (N == 0) return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  const Variant* var = nullptr;
+  int st = check_common(q, k, v, o, lse, d, scale, variant, &var);
+  if (st != FA2_OK) return st;
+  const long long tr = ((long long)N + var->br - 1) / var->br;
+  const long long nbh = (long long)B * H;
+  const long long wg = tr * nbh;
+  // Element offsets are 64-bit in the kernel; the grid and row indices must fit 31 bits.
+  if (wg > 0x7fffffffLL || nbh * (long long)N > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  Params p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.nb = B;
+  p.H = H;
+  p.N = N;
+  p.T = N;
+  p.tr = (int)tr;
+  p.heads_per_xcd = heads_per_xcd(nbh);
+  fill_scale(p, scale);
+  return launch(*var, false, causal != 0, p, (int)wg, stream);
+}
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+            int N, int d, int causal, float scale, void* stream) {
+  return fa2_fwd_variant(q, k, v, o, lse, B, H, N, d, causal, scale, 0, stream);
+}
+
+int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const int* cu_seqlens, int num_seqs, int max_seqlen,
+                           int total_tokens, int H, int d, int causal, float scale, int variant,
+                           void* stream) {
+  if (H <= 0 || num_seqs < 0 || max_seqlen < 0 || total_tokens < 0) return FA2_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
+    return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (!cu_seqlens) return FA2_ERR_NULL_PTR;
+  if (!aligned(cu_seqlens, 4)) return FA2_ERR_MISALIGNED;
+  const Variant* var = nullptr;
+  int st = check_common(q, k, v, o, lse, d, scale, variant, &var);
+  if (st != FA2_OK) return st;
+  const long long tr = ((long long)max_seqlen + var->br - 1) / var->br;
+  const long long nbh = (long long)num_seqs * H;
+  const long long wg = tr * nbh;
+  if (wg > 0x7fffffffLL || (long long)H * total_tokens > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  Params p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.nb = num_seqs;
+  p.H = H;
+  p.N = max_seqlen;
+  p.T = total_tokens;
+  p.tr = (int)tr;
+  p.heads_per_xcd = heads_per_xcd(nbh);
+  fill_scale(p, scale);
+  return launch(*var, true, causal != 0, p, (int)wg, stream);
+}
+
+int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens, int H,
+                   int d, int causal, float scale, void* stream) {
+  return fa2_fwd_varlen_variant(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen,
+                                total_tokens, H, d, causal, scale, 0, stream);
+}
+
+}  // extern "C"

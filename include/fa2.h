@@ -1,0 +1,127 @@
+/*
+ * fa2.h — C ABI of the gfx950 exact-softmax-attention forward library (libfa2.so).
+ *
+ * The operation (per head, per sequence):
+ *     S = scale * Q K^T,  S[i][j] = -inf where causal and j > i,
+ *     P = row-softmax(S),  O = P V,  LSE[i] = log(sum_j exp(S[i][j]))  (natural log)
+ * computed without writing S or P to memory, as in the FlashAttention-2 forward:
+ *   - definition S = QK^T, P = softmax(S), O = PV: "FlashAttention 2: Faster Attention with
+ *     Better Parallelism and Work Partitioning" reading notes (papers.chlience.com), section 1;
+ *     the 1/sqrt(d) scale inside the score: "FlashAttention" (llm-infra-atlas), section 1;
+ *   - the one-pass recurrence with an unscaled accumulator and a single final division, and
+ *     the logsumexp L = m + log(l) as the second output: chlience notes, section 5.2;
+ *     "FlashAttention-2: ..." summary (paper-graph-ui), section 3.4, "Algorithm 1 Walkthrough"
+ *     and "Tweak 2: Store Logsumexp";
+ *   - causal semantics (column index greater than row index is masked) and skipping of tiles
+ *     that lie wholly above the diagonal: paper-graph-ui section 3.4, "Causal masking
+ *     optimization"; chlience notes, section 5.6;
+ *   - packed variable-length batches addressed by cu_seqlens offsets: llm-infra-atlas,
+ *     section 0 (the engineering-interface entry of its reading table).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device pointers (HIP device memory). bf16 tensors are passed as raw 16-bit
+ *     words (bfloat16 bit patterns). q, k, v, o must be 16-byte aligned; lse 4-byte aligned.
+ *   - Ownership: the caller allocates and frees every buffer. The library never allocates,
+ *     frees or retains a pointer, and keeps no mutable global state; calls are reentrant.
+ *   - On success every element of o and lse covered by the call is overwritten (for the
+ *     varlen entry: the rows of every sequence, see below). Inputs are never written.
+ *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
+ *     the call returns without synchronising.
+ *   - Arguments are validated on the host before any HIP call. On any error nothing is
+ *     launched and nothing is written; the return value says why (FA2_* codes below).
+ *   - Problems with zero rows (N == 0, total_tokens == 0 or num_seqs == 0) succeed without a
+ *     launch; their pointers may then be NULL.
+ *   - Results are deterministic: the forward uses no atomics, so a call with the same
+ *     inputs and variant gives bitwise-identical outputs, independent of B and H.
+ */
+#ifndef FA2_H_
+#define FA2_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa2_status {
+  FA2_OK = 0,
+  FA2_ERR_NULL_PTR = 1,            /* a required pointer is NULL */
+  FA2_ERR_BAD_SHAPE = 2,           /* B or H <= 0, N < 0, or inconsistent varlen sizes */
+  FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* d is not 64 or 128 */
+  FA2_ERR_MISALIGNED = 4,          /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
+  FA2_ERR_BAD_SCALE = 5,           /* scale is NaN or infinite */
+  FA2_ERR_NO_DEVICE = 6,           /* no usable HIP device is current */
+  FA2_ERR_LAUNCH = 7,              /* the kernel launch failed (HIP error) */
+  FA2_ERR_BAD_VARIANT = 8,         /* variant index out of range for this d */
+  FA2_ERR_TOO_LARGE = 9            /* the grid or an index would overflow 31 bits */
+};
+
+/*
+ * Fixed-length forward.
+ *   q, k, v : bf16 [B, H, N, d], contiguous (d fastest), read only.
+ *   o       : bf16 [B, H, N, d], contiguous; written with round-to-nearest-even.
+ *   lse     : fp32 [B, H, N]; natural-log logsumexp of each row of S.
+ *   d       : 64 or 128.  causal: 0 or 1 (mask key j > query i).
+ *   scale   : any finite float (typically 1/sqrt(d)); applied to QK^T before the softmax.
+ * Returns FA2_OK or an error code (see above).
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * Packed variable-length forward: num_seqs sequences concatenated along the token axis.
+ *   q, k, v, o : bf16 [H, total_tokens, d] contiguous (each head holds all tokens of all
+ *                sequences back to back).
+ *   lse        : fp32 [H, total_tokens].
+ *   cu_seqlens : DEVICE int32 [num_seqs + 1]; sequence s owns tokens [cu[s], cu[s+1]).
+ *                Expected: cu[0] = 0, non-decreasing, cu[num_seqs] = total_tokens and every
+ *                length <= max_seqlen. The contents are not checked on the host; the kernel
+ *                clamps every offset into [0, total_tokens], so bad offsets never cause an
+ *                out-of-bounds access, but rows outside [0, max_seqlen) of a sequence, and
+ *                tokens covered by no sequence, are then left unwritten.
+ *   max_seqlen : upper bound on the sequence lengths (sizes the grid).
+ *   causal     : mask within each sequence with sequence-local indices.
+ */
+int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                   int H, int d, int causal, float scale, void* stream);
+
+/*
+ * Same as fa2_fwd / fa2_fwd_varlen, with an explicit kernel variant (tile configuration).
+ * variant 0 is the default that fa2_fwd uses; 1 .. fa2_num_variants(d)-1 are alternatives
+ * with identical results up to rounding order. Used by tuning sweeps and tests.
+ */
+int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, int causal, float scale, int variant,
+                    void* stream);
+int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const int* cu_seqlens, int num_seqs, int max_seqlen,
+                           int total_tokens, int H, int d, int causal, float scale,
+                           int variant, void* stream);
+
+/* Number of kernel variants for head dimension d (0 if d is unsupported). Host only. */
+int fa2_num_variants(int d);
+
+/*
+ * Launch geometry of a fixed-length call, computed on the host without touching the GPU:
+ * *num_workgroups = B*H*ceil(N/block_rows), *block_rows = query rows per workgroup,
+ * *block_cols = keys per K/V tile, *lds_bytes = LDS per workgroup. Returns a status code;
+ * outputs may be NULL.
+ */
+int fa2_fwd_geometry(int B, int H, int N, int d, int causal, int variant,
+                     int* num_workgroups, int* block_rows, int* block_cols, int* lds_bytes);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa2_status_str(int status);
+
+/* Static name of a kernel variant ("d128_br128_bc64" ...), or "" if out of range. */
+const char* fa2_variant_name(int d, int variant);
+
+/* ABI version of this header; bumped on any incompatible change. */
+int fa2_abi_version(void);
+
+#define FA2_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H_ */
