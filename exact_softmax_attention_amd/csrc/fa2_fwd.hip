@@ -53,6 +53,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -71,42 +73,39 @@ struct Params {
   int T;                  // tokens per head plane: N, or total_tokens (varlen)
   int tr;                 // row blocks per (batch|sequence, head)
   int heads_per_xcd;      // > 0: XCD-aware workgroup order (nb*H divisible by 8)
-  float c;                // |scale| * log2(e)
+  float c;                // |scale| * log2(e), at least 1e-30
   uint32_t qflip;         // 0x80008000 negates Q (scale < 0), else 0
 };
 
-// Compile-time tile geometry.
+// Compile-time tile geometry. K and V tiles are BC rows of D bf16 (row pitch 2*D bytes,
+// no padding), stored in LDS with their 16-byte chunks permuted by an XOR of low row bits
+// so that the MFMA operand reads below hit distinct banks.
 template <int D, int BC>
 struct Tile {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int BR = 32 * WAVES;        // query rows per workgroup
-  static constexpr int KSTRIDE = D + 8;        // K row pitch in LDS (bf16), +16 B breaks bank aliasing
-  static constexpr int VSTRIDE = BC + 8;       // V^T row pitch in LDS (bf16)
-  static constexpr int KTILE = BC * KSTRIDE;   // bf16 per K stage
-  static constexpr int VTILE = D * VSTRIDE;    // bf16 per V^T stage
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;   // two stages (double buffer)
-  static constexpr int NKB = BC / 32;          // 32-key blocks per tile
-  static constexpr int NKC = D / 16;           // 16-wide contraction steps of QK^T
-  static constexpr int NDB = D / 32;           // 32-wide d blocks of O^T
-  static constexpr int NPC = BC / 16;          // 16-key contraction steps of PV
-  static constexpr int KLOADS = BC * D / 8 / THREADS;    // 16-B K loads per thread and tile
-  static constexpr int VUNITS = BC * D / 32 / THREADS;   // (4 keys x 8 d) V units per thread
-  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(KLOADS >= 1 && KLOADS * 8 * THREADS == BC * D, "K staging must tile exactly");
-  static_assert(VUNITS >= 1 && VUNITS * 32 * THREADS == BC * D, "V staging must tile exactly");
+  static constexpr int BR = 32 * WAVES;             // query rows per workgroup
+  static constexpr int ROWB = 2 * D;                // bytes per K or V row
+  static constexpr int TILEB = BC * ROWB;           // bytes per K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;          // K tile then V tile
+  static constexpr int LDS_BYTES = 2 * STAGEB;      // double buffered
+  static constexpr int DMA_PER_WAVE = TILEB / 1024 / WAVES;  // 1 KB direct loads per wave
+  static constexpr int NKB = BC / 32;               // 32-key blocks per tile
+  static constexpr int NKC = D / 16;                // 16-wide contraction steps of QK^T
+  static constexpr int NDB = D / 32;                // 32-wide d blocks of O^T
+  static constexpr int NPC = BC / 16;               // 16-key contraction steps of PV
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(BC % 32 == 0 && TILEB % (1024 * WAVES) == 0, "tile shape");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+  // Swizzle of K rows: lanes reading 16 consecutive rows at one logical chunk land in 16
+  // distinct 16-byte bank groups.
+  __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  // Swizzle of V rows: a transposed read touches 4 consecutive rows x 2..4 chunks.
+  __device__ static int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 };
 
-// Position of key offset o (0..15) inside a 16-key group of V^T in LDS. It is the order in
-// which the S^T accumulator lanes present keys as PV contraction positions: offsets 4..7
-// and 8..11 trade places (an involution).
-__device__ __forceinline__ int kappa4(int o) {
-  const int g = o >> 2;                              // 4-key group 0..3
-  const int gs = ((g & 1) << 1) | ((g >> 1) & 1);    // swap groups 1 and 2
-  return (gs << 2) | (o & 3);
-}
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -114,6 +113,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 t = {(__bf16)lo, (__bf16)hi};               // round-to-nearest-even
   return __builtin_bit_cast(uint32_t, t);
+}
+
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes at base + voff land at
+// LDS address lds + 16*l. base and lds are wave-uniform. Completion is tracked by vmcnt,
+// which the caller waits on explicitly before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)LDS_PTR(const void, p);
+}
+
+// Maximum over both 32-lane halves (lane l and l^32 hold the two halves of a row's keys).
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Workgroup id -> (batch|sequence * H + head, row block). With the XCD-aware order,
@@ -141,15 +161,23 @@ __device__ __forceinline__ void decode_block(const Params& p, int& bh, int& i) {
   }
 }
 
-template <int D, int BC, bool CAUSAL, bool VARLEN>
+// The softmax bookkeeping either follows the pages' recurrence exactly (the running max is
+// the true running max; the accumulator is rescaled whenever it grows), or, with LAZY, keeps
+// the reference max until a row's tile max exceeds it by more than TAU (base-2 units). Both
+// give the same O = O~ / l and LSE = m + log2 l up to rounding, because the reference value
+// cancels between numerator and denominator; LAZY bounds every P~ entry by 2^TAU.
+constexpr float kLazyTau = 8.0f;
+
+template <int D, int BC, bool CAUSAL, bool VARLEN, bool LAZY>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa2_fwd_kernel(Params p) {
   using TL = Tile<D, BC>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TL::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int l32 = lane & 31;   // MFMA column (query) / A-row index
   const int hl = lane >> 5;    // which 32-lane half
 
@@ -175,8 +203,8 @@ void fa2_fwd_kernel(Params p) {
   if (q0 >= seq_len) return;  // uniform over the workgroup (varlen rows past the end)
 
   const uint16_t* __restrict__ qh = p.q + row0 * D;
-  const uint16_t* __restrict__ kh = p.k + row0 * D;
-  const uint16_t* __restrict__ vh = p.v + row0 * D;
+  const unsigned char* kh = (const unsigned char*)(p.k + row0 * D);
+  const unsigned char* vh = (const unsigned char*)(p.v + row0 * D);
 
   // Key tiles to visit: causal stops after the tile holding this block's last query.
   const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
@@ -194,162 +222,189 @@ void fa2_fwd_kernel(Params p) {
     qf[kc] = as_bf16x8(t);
   }
 
+  // ---- a3: K/V staging, global -> LDS directly (1 KB per wave instruction) -------------
+  // Instruction b of a tile writes LDS bytes [1024 b, 1024 b + 1024); lane l's 16 bytes land
+  // at 1024 b + 16 l, i.e. row r = (1024 b + 16 l) / ROWB, physical chunk pch. The lane
+  // therefore fetches the logical chunk pch ^ swz(r) of global row r.
+  int drow[TL::DMA_PER_WAVE];         // tile row each direct load fills
+  uint32_t koff[TL::DMA_PER_WAVE];    // byte offset inside the tile's global rows (K)
+  uint32_t voff[TL::DMA_PER_WAVE];    // same for V
+#pragma unroll
+  for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+    const int b = wave * TL::DMA_PER_WAVE + d;
+    const int o = b * 1024 + lane * 16;
+    const int r = o / TL::ROWB;
+    const int pch = (o % TL::ROWB) / 16;
+    drow[d] = r;
+    koff[d] = r * TL::ROWB + ((pch ^ TL::kswz(r)) * 16);
+    voff[d] = r * TL::ROWB + ((pch ^ TL::vswz(r)) * 16);
+  }
+
+  auto dma_tile = [&](int j, unsigned char* stage) {
+    const int key0 = j * BC;
+    const unsigned char* kt = kh + (size_t)key0 * TL::ROWB;
+    const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
+    unsigned char* ks = stage;
+    unsigned char* vs = stage + TL::TILEB;
+    const uint32_t ks_a = lds_addr(ks) + wave * TL::DMA_PER_WAVE * 1024;
+    const uint32_t vs_a = lds_addr(vs) + wave * TL::DMA_PER_WAVE * 1024;
+    if (key0 + BC <= seq_len) {
+#pragma unroll
+      for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+        dma16(kt, koff[d], ks_a + d * 1024);
+        dma16(vt, voff[d], vs_a + d * 1024);
+      }
+    } else {
+      // Ragged last tile: rows past the end re-read the last valid row, so every V value
+      // in LDS is finite (its probability is zero after the mask).
+      const int last = seq_len - 1 - key0;
+#pragma unroll
+      for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+        const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * TL::ROWB;
+        dma16(kt, koff[d] - back, ks_a + d * 1024);
+        dma16(vt, voff[d] - back, vs_a + d * 1024);
+      }
+    }
+  };
+
+  // Per-lane LDS read offsets (bytes inside a stage), precomputed once.
+  //  K (A operand of S^T): row kb*32 + l32, logical chunk 2*kc + hl.
+  int kaddr[TL::NKC];
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc)
+    kaddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ TL::kswz(l32)) * 16);
+  //  V^T (A operand of O^T) by two transposed 8-byte reads per fragment: the lane supplies
+  //  row 16c + 8t + 4hl + (lane%16)/4 and columns 32db + 16((lane/16)%2) + 4(lane%4) .. +3,
+  //  and receives keys 16c + 8t + 4hl + 0..3 of column d = 32db + l32.
+  const int vr = 4 * hl + ((lane & 15) >> 2);
+  int vaddr[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) {
+    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    vaddr[db] = vr * TL::ROWB + (((col >> 3) ^ TL::vswz(vr)) * 16) + (col & 7) * 2;
+  }
+
   // ---- running state (fp32, registers) -----------------------------------------------
   f32x16 oacc[TL::NDB];
 #pragma unroll
   for (int db = 0; db < TL::NDB; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY;  // running max of S·c (base-2 domain)
-  float l_run = 0.f;        // this lane's partial running sum (its half of the keys)
+  float m_run = -INFINITY;  // reference max of S·c (base-2 domain) for this lane's query
+  float l_run = 0.f;        // this lane's partial sum (its half of the keys)
 
-  // ---- a3: K/V staging (global -> registers -> LDS, double buffered) ------------------
-  u32x4 kreg[TL::KLOADS];
-  u32x4 vreg[TL::VUNITS][4];
-
-  auto load_tile = [&](int j) {
-    const int kbase = j * BC;
-#pragma unroll
-    for (int r = 0; r < TL::KLOADS; ++r) {
-      const int id = r * TL::THREADS + tid;
-      const int row = id / (D / 8), ch = id % (D / 8);
-      const int key = kbase + row;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (key < seq_len) t = *(const u32x4*)(kh + (size_t)key * D + ch * 8);
-      kreg[r] = t;
-    }
-#pragma unroll
-    for (int u = 0; u < TL::VUNITS; ++u) {
-      const int id = u * TL::THREADS + tid;
-      const int g4 = id % (BC / 4), dc = id / (BC / 4);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = kbase + 4 * g4 + rr;
-        u32x4 t = {0u, 0u, 0u, 0u};   // keys past the end are zero so 0 * V stays finite
-        if (key < seq_len) t = *(const u32x4*)(vh + (size_t)key * D + dc * 8);
-        vreg[u][rr] = t;
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    uint16_t* ks = smem + stage * TL::STAGE;
-    uint16_t* vs = ks + TL::KTILE;
-#pragma unroll
-    for (int r = 0; r < TL::KLOADS; ++r) {
-      const int id = r * TL::THREADS + tid;
-      const int row = id / (D / 8), ch = id % (D / 8);
-      *(u32x4*)(ks + row * TL::KSTRIDE + ch * 8) = kreg[r];
-    }
-#pragma unroll
-    for (int u = 0; u < TL::VUNITS; ++u) {
-      const int id = u * TL::THREADS + tid;
-      const int g4 = id % (BC / 4), dc = id / (BC / 4);
-      const int key0 = 4 * g4;
-      const int pos0 = (key0 & ~15) | kappa4(key0 & 15);
-      // 4 keys x 8 d held as 4 rows of 4 dwords (2 d each) -> 8 d rows of 4 keys.
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t r0 = vreg[u][0][w], r1 = vreg[u][1][w];
-        const uint32_t r2 = vreg[u][2][w], r3 = vreg[u][3][w];
-        u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
-        u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
-        *(u32x2*)(vs + (dc * 8 + 2 * w) * TL::VSTRIDE + pos0) = lo;
-        *(u32x2*)(vs + (dc * 8 + 2 * w + 1) * TL::VSTRIDE + pos0) = hi;
-      }
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) load_tile(j + 1);   // in flight while tile j is computed
-
+  auto compute_tile = [&](int j, const unsigned char* stage) {
     const int key0 = j * BC;
-    const uint16_t* ks = smem + (j & 1) * TL::STAGE;
-    const uint16_t* vs = ks + TL::KTILE;
     // a5: a wave whose rows all precede this tile's first key, or whose rows are all past
-    // the end of the sequence, has nothing to add here (it still joins the barrier).
-    const bool active = (!CAUSAL || key0 <= qw0 + 31) && (qw0 < seq_len);
-    if (active) {
-      // ---- a4: S^T = K_j Q^T --------------------------------------------------------
-      f32x16 s[TL::NKB];
-#pragma unroll
-      for (int kb = 0; kb < TL::NKB; ++kb) {
-        s[kb] = (f32x16){};
-#pragma unroll
-        for (int kc = 0; kc < TL::NKC; ++kc) {
-          const bf16x8 a = *(const bf16x8*)(ks + (kb * 32 + l32) * TL::KSTRIDE + kc * 16 + hl * 8);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
-        }
-      }
+    // the end of the sequence, has nothing to add here.
+    if ((CAUSAL && key0 > qw0 + 31) || qw0 >= seq_len) return;
+    const unsigned char* ks = stage;
+    const unsigned char* vs = stage + TL::TILEB;
 
-      // ---- a5: mask on diagonal and ragged tiles only ---------------------------------
-      const bool need_mask = (CAUSAL && key0 + BC - 1 > qw0) || (key0 + BC > seq_len);
-      if (need_mask) {
+    // ---- a4: S^T = K_j Q^T ----------------------------------------------------------
+    f32x16 s[TL::NKB];
 #pragma unroll
-        for (int kb = 0; kb < TL::NKB; ++kb)
+    for (int kb = 0; kb < TL::NKB; ++kb) {
+      s[kb] = (f32x16){};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool dead = (CAUSAL && key > qrow) || key >= seq_len;
-            if (dead) s[kb][r] = -INFINITY;
-          }
+      for (int kc = 0; kc < TL::NKC; ++kc) {
+        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + kaddr[kc]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
       }
+    }
 
-      // ---- a6: online softmax (fp32) ------------------------------------------------
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < TL::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));            // the other 16 keys of each 32
-      const float mt = (mx == -INFINITY) ? -INFINITY : mx * p.c;
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 on the first tile
-      const bool grew = m_new > m_run;
-      m_run = m_new;
-      l_run *= alpha;
-      // Skip the O~ rescale when no row of the wave changed its max (alpha == 1 exactly).
-      if (__any(grew)) {
-#pragma unroll
-        for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
-      }
-      float rs = 0.f;
+    // ---- a5: mask on diagonal and ragged tiles only -----------------------------------
+    if ((CAUSAL && key0 + BC - 1 > qw0) || key0 + BC > seq_len) {
 #pragma unroll
       for (int kb = 0; kb < TL::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c, -m_use));
-          if (need_mask) e = (s[kb][r] == -INFINITY) ? 0.f : e;
-          s[kb][r] = e;
-          rs += e;
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if ((CAUSAL && key > qrow) || key >= seq_len) s[kb][r] = -INFINITY;
         }
-      l_run += rs;
-
-      // ---- a7: O~^T += V_j^T P~^T ---------------------------------------------------
-#pragma unroll
-      for (int c = 0; c < TL::NPC; ++c) {
-        const f32x16& sb = s[c >> 1];
-        const int r0 = (c & 1) * 8;
-        u32x4 pw = {pack_bf16x2(sb[r0 + 0], sb[r0 + 1]), pack_bf16x2(sb[r0 + 2], sb[r0 + 3]),
-                    pack_bf16x2(sb[r0 + 4], sb[r0 + 5]), pack_bf16x2(sb[r0 + 6], sb[r0 + 7])};
-        const bf16x8 pf = as_bf16x8(pw);
-#pragma unroll
-        for (int db = 0; db < TL::NDB; ++db) {
-          const bf16x8 a = *(const bf16x8*)(vs + (db * 32 + l32) * TL::VSTRIDE + c * 16 + hl * 8);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
-        }
-      }
     }
 
-    if (j + 1 < nt) store_tile((j + 1) & 1);
+    // ---- a6: online softmax (fp32) --------------------------------------------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = halves_max(mx);
+    const float mt = mx * p.c;   // -inf stays -inf (c > 0)
+    if (LAZY) {
+      const bool need = mt > m_run + kLazyTau;    // false when the tile is fully masked
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 if m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+    } else {
+      const float m_new = fmaxf(m_run, mt);
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      const bool grew = m_new > m_run;
+      l_run *= alpha;
+      // Skip the O~ rescale when no row of the wave changed its max (alpha == 1 exactly).
+      if (__builtin_amdgcn_ballot_w64(grew)) {
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
+      }
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c, -m_use));
+        s[kb][r] = e;
+        rs += e;
+      }
+    l_run += rs;
+
+    // ---- a7: O~^T += V_j^T P~^T -----------------------------------------------------
+#pragma unroll
+    for (int c = 0; c < TL::NPC; ++c) {
+      const f32x16& sb = s[c >> 1];
+      const int r0 = (c & 1) * 8;
+      u32x4 pw = {pack_bf16x2(sb[r0 + 0], sb[r0 + 1]), pack_bf16x2(sb[r0 + 2], sb[r0 + 3]),
+                  pack_bf16x2(sb[r0 + 4], sb[r0 + 5]), pack_bf16x2(sb[r0 + 6], sb[r0 + 7])};
+      const bf16x8 pf = as_bf16x8(pw);
+#pragma unroll
+      for (int db = 0; db < TL::NDB; ++db) {
+        const unsigned char* va = vs + vaddr[db] + 16 * c * TL::ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va + 8 * TL::ROWB));
+        const i16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pf,
+                                                           oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- the key/value loop: one barrier per tile ----------------------------------------
+  // Iteration j: wait for this lane's direct loads of tile j, barrier (all of tile j is in
+  // LDS, and every wave has finished tile j-1, whose buffer tile j+1 now overwrites), start
+  // the loads of tile j+1, compute tile j.
+  dma_tile(0, lds0);
+  for (int j = 0; j < nt; j += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (j + 1 < nt) dma_tile(j + 1, lds1);
+    compute_tile(j, lds0);
+    if (j + 1 < nt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 2 < nt) dma_tile(j + 2, lds0);
+      compute_tile(j + 1, lds1);
+    }
   }
 
   // ---- a8: epilogue: O = O~ / l, LSE = (m + log2 l) ln 2 --------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halves_sum(l_run);
   if (qrow < seq_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = p.o + (row0 + (size_t)qrow) * D;
@@ -382,7 +437,7 @@ struct Variant {
   KernelFn varlen[2];  // [causal]
 };
 
-template <int D, int BC>
+template <int D, int BC, bool LAZY>
 Variant make_variant(const char* name) {
   using TL = Tile<D, BC>;
   Variant v;
@@ -391,16 +446,21 @@ Variant make_variant(const char* name) {
   v.br = TL::BR;
   v.bc = BC;
   v.lds = TL::LDS_BYTES;
-  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false>;
-  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false>;
-  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true>;
-  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true>;
+  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false, LAZY>;
+  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false, LAZY>;
+  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true, LAZY>;
+  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true, LAZY>;
   return v;
 }
 
+// Variant 0 of each head dimension is the default. "lazy" keeps a stale reference max
+// until a tile exceeds it by 2^8; "exact" updates the max every tile as the pages do.
 const Variant* variants_for(int d, int* count) {
-  static const Variant v64[] = {make_variant<64, 128>("d64_br128_bc128")};
-  static const Variant v128[] = {make_variant<128, 64>("d128_br128_bc64")};
+  static const Variant v64[] = {make_variant<64, 128, true>("d64_br128_bc128_lazy"),
+                                make_variant<64, 64, true>("d64_br128_bc64_lazy"),
+                                make_variant<64, 128, false>("d64_br128_bc128_exact")};
+  static const Variant v128[] = {make_variant<128, 64, true>("d128_br128_bc64_lazy"),
+                                 make_variant<128, 64, false>("d128_br128_bc64_exact")};
   if (d == 64) {
     *count = (int)(sizeof(v64) / sizeof(v64[0]));
     return v64;
@@ -440,7 +500,9 @@ int launch(const Variant& var, bool varlen, bool causal, Params& p, int num_wg, 
 }
 
 void fill_scale(Params& p, float scale) {
-  p.c = fabsf(scale) * kLog2e;
+  // A zero scale gives uniform attention; a tiny positive c reproduces that (every score
+  // times c rounds to 0) while keeping -inf * c = -inf for masked entries.
+  p.c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
   p.qflip = scale < 0.f ? 0x80008000u : 0u;
 }
 
