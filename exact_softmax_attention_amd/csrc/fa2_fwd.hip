@@ -9,11 +9,11 @@
 //   [PGU] "FlashAttention-2: Faster Attention with Better Parallelism and Work Partitioning",
 //         paper-graph-ui summary
 //
-// One workgroup owns one block of BR = 32*WAVES query rows of one (batch, head) or
-// (sequence, head) pair, and walks the key/value tiles of BC keys in order ([CHL] 5.1, 5.4:
-// query row blocks are the outer, parallel loop; key/value blocks the inner, sequential
-// one). Each 64-lane wave owns 32 whole query rows, so no statistic is ever shared between
-// waves ([CHL] 5.5 split-Q; [PGU] 3.4 "warp-level work partitioning"). Per tile and wave:
+// One workgroup owns a block of query rows of one (batch, head) or (sequence, head) pair
+// and walks the key/value tiles of BC keys in order ([CHL] 5.1, 5.4: query row blocks are
+// the outer, parallel loop; key/value blocks the inner, sequential one). Each 64-lane wave
+// owns 32 whole query rows, so no statistic is ever shared between waves ([CHL] 5.5
+// split-Q; [PGU] 3.4 "warp-level work partitioning"). Per tile and wave:
 //
 //   S^T  = K_j Q_i^T          bf16 MFMA 32x32x16, fp32 accumulate      (a4)
 //   mask                      only on diagonal / ragged tiles            (a5)
@@ -24,21 +24,28 @@
 // "Algorithm 1 Walkthrough"; the rescale multiplies by 2^(m-m') <= 1 as in the erratum of
 // [LAN] "减少非矩阵乘法运算"). c = scale·log2(e) folds the softmax scale into the base-2
 // exponential the hardware provides (v_exp_f32 computes 2^x); [ATL] 2 notes the upstream
-// rescale also uses exp2.
+// rescale also uses exp2. The reference max m may lag the true running max (kLazy,
+// kOptimistic below); the result is the same because m cancels in O~/l and in m + log2 l.
 //
 // Why S^T and not S: a 32x32 MFMA result gives each lane one column and 16 rows. Computing
 // S^T = K Q^T puts one query per lane column, so a lane holds 16 keys of a single query per
 // 32-key block: the row max and row sum are in-lane, plus one exchange between the two
-// 32-lane halves. The same lane layout is exactly the B operand the PV product needs
-// (O^T = V^T P^T, one query per lane column, 8 consecutive contraction positions per lane),
-// so P~ never leaves registers. The contraction positions of that B operand map to keys
-// through the fixed permutation kappa below; V^T is stored in LDS in that permuted key order
-// so that its A-operand fragment is one contiguous 16-byte LDS read.
+// 32-lane halves (v_permlane32_swap). The same lane layout is exactly the B operand the PV
+// product needs (O^T = V^T P^T, one query per lane column, 8 contraction positions per lane),
+// so P~ never leaves registers. For contraction step c, operand position 8h + 4t + e (h =
+// lane half, t = 0/1, e = 0..3) carries key 16c + 8t + 4h + e on both sides; the V^T operand
+// is gathered from the row-major V tile in LDS with two LDS transpose reads
+// (ds_read_b64_tr_b16) in exactly that key order.
+//
+// K and V tiles move from global memory straight into LDS (global_load_lds_dwordx4), with
+// their 16-byte chunks XOR-swizzled by row so that every operand read is bank-conflict free.
 //
 // MFMA lane layouts used (v_mfma_f32_32x32x16_bf16, wave64, lane l, element e):
 //   A[m][k]: m = l % 32, k = 8*(l / 32) + e          (8 bf16 per lane)
 //   B[k][n]: n = l % 32, k = 8*(l / 32) + e          (8 bf16 per lane)
 //   C[m][n]: n = l % 32, m = 8*(r / 4) + 4*(l / 32) + r % 4, r = 0..15   (16 fp32 per lane)
+// ds_read_b64_tr_b16 (per 16-lane group, lane j of the group receives element j % 4 of the
+// 8-byte rows addressed by lanes 4e + (j % 16) / 4, e = 0..3).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -161,14 +168,23 @@ __device__ __forceinline__ void decode_block(const Params& p, int& bh, int& i) {
   }
 }
 
-// The softmax bookkeeping either follows the pages' recurrence exactly (the running max is
-// the true running max; the accumulator is rescaled whenever it grows), or, with LAZY, keeps
-// the reference max until a row's tile max exceeds it by more than TAU (base-2 units). Both
-// give the same O = O~ / l and LSE = m + log2 l up to rounding, because the reference value
-// cancels between numerator and denominator; LAZY bounds every P~ entry by 2^TAU.
+// Softmax bookkeeping modes. All three give the same O = O~ / l and LSE = m + log2 l up to
+// rounding, because the reference value m cancels between numerator and denominator; they
+// differ in how often the row max is computed and the accumulator rescaled.
+//   kExact:      the pages' recurrence: m = max(m, rowmax) every tile, rescale when it grows.
+//   kLazy:       rowmax every tile, but m only moves when a tile exceeds it by 2^kLazyTau.
+//   kOptimistic: P~ is formed with the current m first; only when a lane's tile sum exceeds
+//                2^kLazyTau (or on the row's first tile) is the true row max taken, the
+//                state rescaled and P~ formed again. m only grows and never passes the
+//                true running max, so no entry underflows earlier than with kExact, and
+//                every P~ entry is at most 2^kLazyTau.
+enum { kExact = 0, kLazy = 1, kOptimistic = 2 };
 constexpr float kLazyTau = 8.0f;
+constexpr float kOptLimit = 256.0f;   // 2^kLazyTau
 
-template <int D, int BC, bool CAUSAL, bool VARLEN, bool LAZY>
+// LA: how many operand fragments are read from LDS ahead of the MFMA that consumes them
+// (0 leaves the order to the compiler's scheduler).
+template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa2_fwd_kernel(Params p) {
   using TL = Tile<D, BC>;
@@ -222,7 +238,7 @@ void fa2_fwd_kernel(Params p) {
     qf[kc] = as_bf16x8(t);
   }
 
-  // ---- a3: K/V staging, global -> LDS directly (1 KB per wave instruction) -------------
+  // ---- a3: K/V staging: global -> LDS directly (1 KB per wave instruction) ------------
   // Instruction b of a tile writes LDS bytes [1024 b, 1024 b + 1024); lane l's 16 bytes land
   // at 1024 b + 16 l, i.e. row r = (1024 b + 16 l) / ROWB, physical chunk pch. The lane
   // therefore fetches the logical chunk pch ^ swz(r) of global row r.
@@ -244,10 +260,8 @@ void fa2_fwd_kernel(Params p) {
     const int key0 = j * BC;
     const unsigned char* kt = kh + (size_t)key0 * TL::ROWB;
     const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
-    unsigned char* ks = stage;
-    unsigned char* vs = stage + TL::TILEB;
-    const uint32_t ks_a = lds_addr(ks) + wave * TL::DMA_PER_WAVE * 1024;
-    const uint32_t vs_a = lds_addr(vs) + wave * TL::DMA_PER_WAVE * 1024;
+    const uint32_t ks_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
+    const uint32_t vs_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
     if (key0 + BC <= seq_len) {
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
@@ -255,8 +269,8 @@ void fa2_fwd_kernel(Params p) {
         dma16(vt, voff[d], vs_a + d * 1024);
       }
     } else {
-      // Ragged last tile: rows past the end re-read the last valid row, so every V value
-      // in LDS is finite (its probability is zero after the mask).
+      // Ragged last tile: rows past the end re-read the last valid row, so every value in
+      // LDS is finite (its probability is zero after the mask).
       const int last = seq_len - 1 - key0;
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
@@ -273,15 +287,15 @@ void fa2_fwd_kernel(Params p) {
 #pragma unroll
   for (int kc = 0; kc < TL::NKC; ++kc)
     kaddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ TL::kswz(l32)) * 16);
-  //  V^T (A operand of O^T) by two transposed 8-byte reads per fragment: the lane supplies
-  //  row 16c + 8t + 4hl + (lane%16)/4 and columns 32db + 16((lane/16)%2) + 4(lane%4) .. +3,
-  //  and receives keys 16c + 8t + 4hl + 0..3 of column d = 32db + l32.
+  //  V^T (A operand of O^T) by two transposed 8-byte reads per fragment from row-major V:
+  //  the lane supplies row 16c + 8t + 4hl + (lane%16)/4 and columns 32db + 16((lane/16)%2) +
+  //  4(lane%4) .. +3, and receives keys 16c + 8t + 4hl + 0..3 of column d = 32db + l32.
   const int vr = 4 * hl + ((lane & 15) >> 2);
   int vaddr[TL::NDB];
 #pragma unroll
   for (int db = 0; db < TL::NDB; ++db) {
     const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    vaddr[db] = vr * TL::ROWB + (((col >> 3) ^ TL::vswz(vr)) * 16) + (col & 7) * 2;
+    vaddr[db] = TL::TILEB + vr * TL::ROWB + (((col >> 3) ^ TL::vswz(vr)) * 16) + (col & 7) * 2;
   }
 
   // ---- running state (fp32, registers) -----------------------------------------------
@@ -297,7 +311,6 @@ void fa2_fwd_kernel(Params p) {
     // the end of the sequence, has nothing to add here.
     if ((CAUSAL && key0 > qw0 + 31) || qw0 >= seq_len) return;
     const unsigned char* ks = stage;
-    const unsigned char* vs = stage + TL::TILEB;
 
     // ---- a4: S^T = K_j Q^T ----------------------------------------------------------
     f32x16 s[TL::NKB];
@@ -310,38 +323,86 @@ void fa2_fwd_kernel(Params p) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
       }
     }
+    if constexpr (LA > 0) {
+      // LDS latency: keep LA fragment reads in flight ahead of the MFMA chain.
+      constexpr int NF = TL::NKB * TL::NKC;
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
 
     // ---- a5: mask on diagonal and ragged tiles only -----------------------------------
+    // Entry (kb, r) of this lane is key key0 + koffs with koffs = kb*32 + 8*(r/4) + 4*hl + r%4.
+    // It is dead when koffs - 4*hl exceeds thr (causal: key > query; ragged: key >= length),
+    // a per-lane threshold; the sign of thr - const selects -inf with one bitfield insert.
     if ((CAUSAL && key0 + BC - 1 > qw0) || key0 + BC > seq_len) {
+      int thr = seq_len - 1 - key0 - 4 * hl;
+      if (CAUSAL) thr = min(thr, qrow - key0 - 4 * hl);
 #pragma unroll
       for (int kb = 0; kb < TL::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if ((CAUSAL && key > qrow) || key >= seq_len) s[kb][r] = -INFINITY;
+          const int kc = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const uint32_t dead = (uint32_t)((thr - kc) >> 31);          // all ones if kc > thr
+          const uint32_t bits = __float_as_uint(s[kb][r]);
+          s[kb][r] = __uint_as_float((bits & ~dead) | (0xff800000u & dead));   // -inf
         }
     }
 
     // ---- a6: online softmax (fp32) --------------------------------------------------
-    float mx = -INFINITY;
+    // pw[c] holds P~ for PV contraction step c as 4 packed bf16 pairs.
+    u32x4 pw[TL::NPC];
+    auto form_p = [&](float m_ref) {
+      float rsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < TL::NKB; ++kb)
+      for (int c = 0; c < TL::NPC; ++c) {
+        const int kb = c >> 1, r0 = (c & 1) * 8;
+        float e[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = halves_max(mx);
-    const float mt = mx * p.c;   // -inf stays -inf (c > 0)
-    if (LAZY) {
-      const bool need = mt > m_run + kLazyTau;    // false when the tile is fully masked
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mt : m_run;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 if m_run = -inf
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
-        m_run = m_new;
+        for (int u = 0; u < 8; ++u) {
+          e[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + u], p.c, -m_ref));
+          rsum += e[u];
+        }
+        pw[c] = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                        pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
       }
+      return rsum;
+    };
+    auto tile_max = [&]() {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      return halves_max(mx) * p.c;   // -inf stays -inf (c > 0)
+    };
+    // Move the reference max to m_new (per lane), rescaling l and O~ by 2^(m_run - m_new).
+    auto rescale_to = [&](float m_new) {
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);   // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    };
+    float rs;
+    if (MODE == kOptimistic) {
+      rs = form_p(m_run == -INFINITY ? 0.f : m_run);
+      // Slow path: the row's first tile, or a tile whose P~ grew too large (rs may be inf).
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kOptLimit) || m_run == -INFINITY)) {
+        rescale_to(fmaxf(m_run, tile_max()));
+        rs = form_p(m_run == -INFINITY ? 0.f : m_run);
+      }
+    } else if (MODE == kLazy) {
+      const float mt = tile_max();
+      const bool need = mt > m_run + kLazyTau;    // false when the tile is fully masked
+      if (__builtin_amdgcn_ballot_w64(need)) rescale_to(need ? mt : m_run);
+      rs = form_p(m_run == -INFINITY ? 0.f : m_run);
     } else {
-      const float m_new = fmaxf(m_run, mt);
+      const float m_new = fmaxf(m_run, tile_max());
       const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
       const bool grew = m_new > m_run;
@@ -352,58 +413,353 @@ void fa2_fwd_kernel(Params p) {
         for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
       }
       m_run = m_new;
+      rs = form_p(m_ref);
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < TL::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c, -m_use));
-        s[kb][r] = e;
-        rs += e;
-      }
     l_run += rs;
 
     // ---- a7: O~^T += V_j^T P~^T -----------------------------------------------------
 #pragma unroll
     for (int c = 0; c < TL::NPC; ++c) {
-      const f32x16& sb = s[c >> 1];
-      const int r0 = (c & 1) * 8;
-      u32x4 pw = {pack_bf16x2(sb[r0 + 0], sb[r0 + 1]), pack_bf16x2(sb[r0 + 2], sb[r0 + 3]),
-                  pack_bf16x2(sb[r0 + 4], sb[r0 + 5]), pack_bf16x2(sb[r0 + 6], sb[r0 + 7])};
-      const bf16x8 pf = as_bf16x8(pw);
+      const bf16x8 pf = as_bf16x8(pw[c]);
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db) {
-        const unsigned char* va = vs + vaddr[db] + 16 * c * TL::ROWB;
+        const unsigned char* va = stage + vaddr[db] + 16 * c * TL::ROWB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va + 8 * TL::ROWB));
-        const i16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pf,
-                                                           oacc[db], 0, 0, 0);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
+      }
+    }
+    if constexpr (LA > 0) {
+      constexpr int NF = TL::NPC * TL::NDB;       // V^T fragments per tile
+      constexpr int RPF = 2;                      // transposed LDS reads per fragment
+      __builtin_amdgcn_sched_group_barrier(0x100, LA * RPF, 0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
       }
     }
   };
 
   // ---- the key/value loop: one barrier per tile ----------------------------------------
-  // Iteration j: wait for this lane's direct loads of tile j, barrier (all of tile j is in
-  // LDS, and every wave has finished tile j-1, whose buffer tile j+1 now overwrites), start
-  // the loads of tile j+1, compute tile j.
-  dma_tile(0, lds0);
-  for (int j = 0; j < nt; j += 2) {
+  // Iteration j begins after a barrier that publishes tile j in its stage and certifies
+  // every wave has finished tile j-1, whose stage now takes tile j+1: its direct loads
+  // start, tile j is computed, the loads are waited for, and the next barrier follows.
+  auto iteration = [&](int j, unsigned char* cur, unsigned char* nxt) {
+    if (j + 1 < nt) dma_tile(j + 1, nxt);
+    compute_tile(j, cur);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < nt) dma_tile(j + 1, lds1);
-    compute_tile(j, lds0);
-    if (j + 1 < nt) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (j + 2 < nt) dma_tile(j + 2, lds0);
-      compute_tile(j + 1, lds1);
-    }
+  };
+  dma_tile(0, lds0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < nt; j += 2) {
+    iteration(j, lds0, lds1);
+    if (j + 1 < nt) iteration(j + 1, lds1, lds0);
   }
 
   // ---- a8: epilogue: O = O~ / l, LSE = (m + log2 l) ln 2 --------------------------------
+  const float l_tot = halves_sum(l_run);
+  if (qrow < seq_len) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = p.o + (row0 + (size_t)qrow) * D;
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
+                   pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+        *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
+      }
+    if (hl == 0) {
+      p.lse[row0 + (size_t)qrow] =
+          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// ---- ping-pong variant ---------------------------------------------------------------
+// Same method and per-wave tiles (32 query rows per wave, S^T / O^T formulation), with eight
+// waves per workgroup (256 query rows) arranged so that the two waves sharing a SIMD work in
+// opposite phases: while one runs matrix-core work (the PV product of tile j-1 and the S
+// product of tile j), the other runs the softmax VALU work of a tile, and all eight waves
+// meet at a barrier between phases. Every wave runs the same sequence
+//     [MFMA phase: PV(j-1), S(j)]  barrier  [VALU phase: softmax(j)]  barrier
+// and group B (waves 4..7) executes one extra barrier before it, group A (waves 0..3) one
+// after it, so B trails A by exactly one phase and their MFMA and VALU phases alternate.
+// K/V tiles are staged by direct loads into a ring of four LDS stages. A wave issues its
+// share of tile j+2 at the start of its MFMA phase j and waits for tile j+1 at the end of
+// it. In global phases, tile t is issued in phase 2t-4 (group A) or 2t-3 (group B), is
+// complete by the end of phase 2t-1, and is last read in phase 2t+3 (group B's PV(t)), so
+// the stage of tile t-4, last read in phase 2t-5, is free.
+template <int D, int BC>
+struct TilePP {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BR = 32 * WAVES;
+  static constexpr int ROWB = 2 * D;
+  static constexpr int TILEB = BC * ROWB;
+  static constexpr int STAGEB = 2 * TILEB;                  // K tile then V tile
+  static constexpr int NSTAGE = 4;
+  static constexpr int LDS_BYTES = NSTAGE * STAGEB;
+  static constexpr int DMA_PER_WAVE = TILEB / 1024 / WAVES;
+  static constexpr int NKB = BC / 32;
+  static constexpr int NKC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int NPC = BC / 16;
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(BC % 32 == 0 && TILEB % (1024 * WAVES) == 0 && DMA_PER_WAVE >= 1, "tile shape");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  __device__ static int kswz(int row) { return Tile<D, BC>::kswz(row); }
+  __device__ static int vswz(int row) { return Tile<D, BC>::vswz(row); }
+};
+
+template <int D, int BC, bool CAUSAL, bool VARLEN, int LA>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fa2_fwd_kernel_pp(Params p) {
+  using TL = TilePP<D, BC>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[TL::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;    // 0: group A, 1: group B (one phase behind)
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  // ---- a1: work decode ----------------------------------------------------------------
+  int bh, i;
+  decode_block<CAUSAL>(p, bh, i);
+  const int bi = bh / p.H;
+  const int h = bh - bi * p.H;
+  int seq_len;
+  size_t row0;
+  if (VARLEN) {
+    int a = p.cu_seqlens[bi];
+    int e = p.cu_seqlens[bi + 1];
+    a = min(max(a, 0), p.T);
+    e = min(max(e, a), p.T);
+    seq_len = e - a;
+    row0 = (size_t)h * (size_t)p.T + (size_t)a;
+  } else {
+    seq_len = p.N;
+    row0 = (size_t)bh * (size_t)p.N;
+  }
+  const int q0 = i * TL::BR;
+  if (q0 >= seq_len) return;
+
+  const uint16_t* __restrict__ qh = p.q + row0 * D;
+  const unsigned char* kh = (const unsigned char*)(p.k + row0 * D);
+  const unsigned char* vh = (const unsigned char*)(p.v + row0 * D);
+  const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
+  const int nt = (kv_end + BC - 1) / BC;
+
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  // Tiles this wave computes: causal tile j matters iff its first key <= the wave's last row.
+  const int ntw = (qw0 >= seq_len) ? 0 : (CAUSAL ? min(nt, (qw0 + 31) / BC + 1) : nt);
+
+  // ---- a2: Q^T fragments ----------------------------------------------------------------
+  bf16x8 qf[TL::NKC];
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+    if (qrow < seq_len) t = *(const u32x4*)(qh + (size_t)qrow * D + kc * 16 + hl * 8);
+    t ^= p.qflip;
+    qf[kc] = as_bf16x8(t);
+  }
+
+  // ---- a3: direct global -> LDS staging into the stage ring -----------------------------
+  int drow[TL::DMA_PER_WAVE];
+  uint32_t koff[TL::DMA_PER_WAVE];
+  uint32_t voff[TL::DMA_PER_WAVE];
+#pragma unroll
+  for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+    const int b = wave * TL::DMA_PER_WAVE + d;
+    const int o = b * 1024 + lane * 16;
+    const int r = o / TL::ROWB;
+    const int pch = (o % TL::ROWB) / 16;
+    drow[d] = r;
+    koff[d] = r * TL::ROWB + ((pch ^ TL::kswz(r)) * 16);
+    voff[d] = r * TL::ROWB + ((pch ^ TL::vswz(r)) * 16);
+  }
+  const uint32_t lds_base = lds_addr(lds);
+  auto dma_tile = [&](int j) {
+    const int key0 = j * BC;
+    const unsigned char* kt = kh + (size_t)key0 * TL::ROWB;
+    const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
+    const uint32_t st = lds_base + (uint32_t)(j & (TL::NSTAGE - 1)) * TL::STAGEB;
+    const uint32_t ks_a = st + wave * TL::DMA_PER_WAVE * 1024;
+    const uint32_t vs_a = st + TL::TILEB + wave * TL::DMA_PER_WAVE * 1024;
+    if (key0 + BC <= seq_len) {
+#pragma unroll
+      for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+        dma16(kt, koff[d], ks_a + d * 1024);
+        dma16(vt, voff[d], vs_a + d * 1024);
+      }
+    } else {
+      const int last = seq_len - 1 - key0;   // rows past the end re-read the last valid row
+#pragma unroll
+      for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+        const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * TL::ROWB;
+        dma16(kt, koff[d] - back, ks_a + d * 1024);
+        dma16(vt, voff[d] - back, vs_a + d * 1024);
+      }
+    }
+  };
+
+  int kaddr[TL::NKC];
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc)
+    kaddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ TL::kswz(l32)) * 16);
+  const int vr = 4 * hl + ((lane & 15) >> 2);
+  int vaddr[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) {
+    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    vaddr[db] = TL::TILEB + vr * TL::ROWB + (((col >> 3) ^ TL::vswz(vr)) * 16) + (col & 7) * 2;
+  }
+
+  // ---- running state ------------------------------------------------------------------
+  f32x16 oacc[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) oacc[db] = (f32x16){};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 s[TL::NKB];      // S of the tile the next VALU phase works on
+  u32x4 pw[TL::NPC];      // P~ (bf16 pairs) of the tile the next MFMA phase multiplies
+
+  auto stage_ptr = [&](int j) { return lds + (j & (TL::NSTAGE - 1)) * TL::STAGEB; };
+
+  // MFMA phase: PV of tile jp (if any) and S of tile js (if any), interleaved.
+  auto mfma_phase = [&](int jp, int js) {
+    const bool do_pv = jp >= 0 && jp < ntw;
+    const bool do_s = js < ntw;
+    if (do_pv) {
+      const unsigned char* st = stage_ptr(jp);
+#pragma unroll
+      for (int c = 0; c < TL::NPC; ++c) {
+        const bf16x8 pf = as_bf16x8(pw[c]);
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db) {
+          const unsigned char* va = st + vaddr[db] + 16 * c * TL::ROWB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va + 8 * TL::ROWB));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
+        }
+      }
+      if constexpr (LA > 0) {
+        constexpr int NF = TL::NPC * TL::NDB;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+    }
+    if (do_s) {
+      const unsigned char* ks = stage_ptr(js);
+#pragma unroll
+      for (int kb = 0; kb < TL::NKB; ++kb) {
+        s[kb] = (f32x16){};
+#pragma unroll
+        for (int kc = 0; kc < TL::NKC; ++kc) {
+          const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + kaddr[kc]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+        }
+      }
+      if constexpr (LA > 0) {
+        constexpr int NF = TL::NKB * TL::NKC;
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+    }
+  };
+
+  // VALU phase: mask and online softmax of tile j (lazy reference max: the tile's row max
+  // is taken, and m, l and O~ move only when it exceeds m by 2^kLazyTau). P~ is formed in
+  // place in fp32, then packed to bf16 for the next MFMA phase.
+  auto valu_phase = [&](int j) {
+    if (j >= ntw) return;
+    const int key0 = j * BC;
+    if ((CAUSAL && key0 + BC - 1 > qw0) || key0 + BC > seq_len) {
+      int thr = seq_len - 1 - key0 - 4 * hl;
+      if (CAUSAL) thr = min(thr, qrow - key0 - 4 * hl);
+#pragma unroll
+      for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kc = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const uint32_t dead = (uint32_t)((thr - kc) >> 31);
+          const uint32_t bits = __float_as_uint(s[kb][r]);
+          s[kb][r] = __uint_as_float((bits & ~dead) | (0xff800000u & dead));
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float mt = halves_max(mx) * p.c;
+    const bool need = mt > m_run + kLazyTau;   // false for a fully masked tile
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 if m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+    float rsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < TL::NPC; ++c) {
+      const int kb = c >> 1, r0 = (c & 1) * 8;
+      float e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        e[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + u], p.c, -m_ref));
+        rsum += e[u];
+      }
+      pw[c] = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                      pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+    }
+    l_run += rsum;
+  };
+
+  // ---- the phase loop ------------------------------------------------------------------
+  dma_tile(0);
+  if (nt > 1) dma_tile(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (grp == 1) __syncthreads();        // group B trails group A by one phase
+  for (int j = 0; j <= nt; ++j) {
+    const bool more = j + 2 < nt;
+    if (more) dma_tile(j + 2);
+    mfma_phase(j - 1, j);
+    // Tile j+1 must be in LDS before the barrier; tile j+2's loads may stay in flight.
+    if (more) {
+      if constexpr (2 * TL::DMA_PER_WAVE == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if constexpr (2 * TL::DMA_PER_WAVE == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    valu_phase(j);
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();
+
+  // ---- a8: epilogue ------------------------------------------------------------------
   const float l_tot = halves_sum(l_run);
   if (qrow < seq_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -433,34 +789,59 @@ struct Variant {
   int br;
   int bc;
   int lds;
+  int threads;
   KernelFn fixed[2];   // [causal]
   KernelFn varlen[2];  // [causal]
 };
 
-template <int D, int BC, bool LAZY>
+template <int D, int BC, int MODE, int LA = 0>
 Variant make_variant(const char* name) {
   using TL = Tile<D, BC>;
   Variant v;
+  v.threads = TL::THREADS;
   v.name = name;
   v.d = D;
   v.br = TL::BR;
   v.bc = BC;
   v.lds = TL::LDS_BYTES;
-  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false, LAZY>;
-  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false, LAZY>;
-  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true, LAZY>;
-  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true, LAZY>;
+  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false, MODE, LA>;
+  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false, MODE, LA>;
+  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true, MODE, LA>;
+  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true, MODE, LA>;
   return v;
 }
 
-// Variant 0 of each head dimension is the default. "lazy" keeps a stale reference max
-// until a tile exceeds it by 2^8; "exact" updates the max every tile as the pages do.
+template <int D, int BC, int LA>
+Variant make_variant_pp(const char* name) {
+  using TL = TilePP<D, BC>;
+  Variant v;
+  v.threads = TL::THREADS;
+  v.name = name;
+  v.d = D;
+  v.br = TL::BR;
+  v.bc = BC;
+  v.lds = TL::LDS_BYTES;
+  v.fixed[0] = (KernelFn)&fa2_fwd_kernel_pp<D, BC, false, false, LA>;
+  v.fixed[1] = (KernelFn)&fa2_fwd_kernel_pp<D, BC, true, false, LA>;
+  v.varlen[0] = (KernelFn)&fa2_fwd_kernel_pp<D, BC, false, true, LA>;
+  v.varlen[1] = (KernelFn)&fa2_fwd_kernel_pp<D, BC, true, true, LA>;
+  return v;
+}
+
+// Variant 0 of each head dimension is the default; the others exist for tuning and tests.
 const Variant* variants_for(int d, int* count) {
-  static const Variant v64[] = {make_variant<64, 128, true>("d64_br128_bc128_lazy"),
-                                make_variant<64, 64, true>("d64_br128_bc64_lazy"),
-                                make_variant<64, 128, false>("d64_br128_bc128_exact")};
-  static const Variant v128[] = {make_variant<128, 64, true>("d128_br128_bc64_lazy"),
-                                 make_variant<128, 64, false>("d128_br128_bc64_exact")};
+  static const Variant v64[] = {
+      make_variant<64, 128, kOptimistic, 4>("d64_bc128_opt_la4"),
+      make_variant<64, 128, kOptimistic>("d64_bc128_opt"),
+      make_variant<64, 128, kLazy, 4>("d64_bc128_lazy_la4"),
+      make_variant<64, 128, kExact>("d64_bc128_exact"),
+      make_variant_pp<64, 64, 4>("d64_pp_bc64_la4")};
+  static const Variant v128[] = {
+      make_variant<128, 64, kOptimistic, 4>("d128_bc64_opt_la4"),
+      make_variant<128, 64, kOptimistic>("d128_bc64_opt"),
+      make_variant<128, 64, kLazy, 4>("d128_bc64_lazy_la4"),
+      make_variant<128, 64, kExact>("d128_bc64_exact"),
+      make_variant_pp<128, 64, 4>("d128_pp_bc64_la4")};
   if (d == 64) {
     *count = (int)(sizeof(v64) / sizeof(v64[0]));
     return v64;
@@ -494,7 +875,7 @@ int launch(const Variant& var, bool varlen, bool causal, Params& p, int num_wg, 
   if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
   KernelFn fn = varlen ? var.varlen[causal ? 1 : 0] : var.fixed[causal ? 1 : 0];
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)num_wg), dim3(256), args, 0,
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)num_wg), dim3((unsigned)var.threads), args, 0,
                                  (hipStream_t)stream);
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }

@@ -31,7 +31,7 @@ Sources for each line:
   * causal: entries with column index greater than row index are -inf:
     paper-graph-ui §3.4, "Causal masking optimization"; chlience notes §5.6.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * the scale multiplies Q K^T before the softmax, and LSE is taken over the
     scaled scores, in natural log;
   * the scale is the float32 value the kernel receives, widened to fp64;

@@ -124,7 +124,7 @@ def test_fwd_empty_is_ok_without_pointers():
     (dict(cu=None), 1), (dict(q=None), 1), (dict(lse=None), 1),
     (dict(H=0), 2), (dict(S=-1), 2), (dict(maxlen=-1), 2), (dict(T=-1), 2),
     (dict(d=80), 3), (dict(cu=FAKE + 2), 4), (dict(k=FAKE + 4), 4),
-    (dict(scale=float("nan")), 5), (dict(variant=7), 8),
+    (dict(scale=float("nan")), 5), (dict(variant=999), 8),
     (dict(S=1 << 20, maxlen=1 << 20, T=1 << 20, H=64), 9),
 ])
 def test_varlen_validation(kwargs, code):
