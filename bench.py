@@ -47,12 +47,14 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(w, lengths=None) -> int:
-    """Q, K, V read once and O written once (bf16), LSE written once (fp32)."""
+def algorithmic_bytes(w, lengths=None, kv_heads=None) -> int:
+    """Q, K, V read once and O written once (bf16), LSE written once (fp32); K and V have
+    kv_heads heads (grouped-query attention), H by default."""
+    hk = w.H if kv_heads is None else kv_heads
     if w.varlen:
         T = sum(lengths)
-        return 8 * w.H * T * w.d + 4 * w.H * T
-    return 8 * w.B * w.H * w.N * w.d + 4 * w.B * w.H * w.N
+        return 4 * (w.H + hk) * T * w.d + 4 * w.H * T
+    return 4 * w.B * (w.H + hk) * w.N * w.d + 4 * w.B * w.H * w.N
 
 
 def load_traffic():
@@ -107,6 +109,18 @@ def run(args):
         def step():
             fa2.fwd_varlen(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o, lse=lse,
                            variant=args.variant)
+    elif args.kv_heads:
+        from synthetic import make_qkv
+        if w.H % args.kv_heads:
+            raise SystemExit(f"--kv-heads {args.kv_heads} must divide H={w.H}")
+        q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.seed, w.k_scale, H_kv=args.kv_heads)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        flops = metric_flops(w.B, w.H, w.N, w.d, w.causal)
+
+        def step():
+            fa2.fwd_gqa(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, variant=args.variant)
     else:
         q, k, v = workload_inputs(w)
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -140,7 +154,7 @@ def run(args):
     tflops = flops / (ms * 1e-3) / 1e12
 
     traffic = None
-    t = load_traffic()
+    t = load_traffic() if (w.name == "c4" and not args.kv_heads and args.variant == 0) else None
     if t is not None:
         traffic = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
@@ -149,6 +163,9 @@ def run(args):
               "causal": w.causal, "kernel_variant": variant}
     if w.varlen:
         config.update({"lengths": lengths, "total_tokens": sum(lengths)})
+    if args.kv_heads:
+        config.update({"workload": f"{w.name} with grouped-query K/V: {w.description}, "
+                                   f"{args.kv_heads} key/value heads", "H_kv": args.kv_heads})
     out = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak",
         "value": round(tflops, 2),
@@ -159,7 +176,8 @@ def run(args):
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3) if w.name == "c4" else None),
+        "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3)
+                        if w.name == "c4" and not args.kv_heads else None),
         "dtype": "bf16",
         "data": "synthetic",
         "config": config,
@@ -171,13 +189,14 @@ def run(args):
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": algorithmic_bytes(w, lengths),
+            "algorithmic_bytes": algorithmic_bytes(w, lengths, args.kv_heads or None),
             "flops_per_launch": flops,
             "kernel_ms": round(ms, 5),
         },
     }
     if args.cpu_baseline_heads > 0:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_baseline_heads) if not w.varlen else None
+        out["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_baseline_heads)
+                               if not (w.varlen or args.kv_heads) else None)
     print(json.dumps(out), flush=True)
 
 
@@ -220,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="grouped-query attention: K/V with this many heads (must divide H; 0: H)")
     ap.add_argument("--cpu-baseline-heads", type=int, default=8,
                     help="(batch, head) pairs of the workload the CPU oracle is timed on (0: skip)")
     ap.add_argument("--calib-copy", action="store_true",

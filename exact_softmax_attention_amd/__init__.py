@@ -12,7 +12,9 @@ from ._lib import (
     Fa2Error,
     STATUS,
     fwd,
+    fwd_gqa,
     fwd_varlen,
+    fwd_varlen_gqa,
     geometry,
     lib_path,
     load_library,
@@ -25,7 +27,9 @@ __all__ = [
     "Fa2Error",
     "STATUS",
     "fwd",
+    "fwd_gqa",
     "fwd_varlen",
+    "fwd_varlen_gqa",
     "geometry",
     "lib_path",
     "load_library",

@@ -30,6 +30,8 @@ _SIGNATURES = {
     "fa2_fwd_variant": ([_c_void_p] * 5 + [_c_int] * 5 + [_c_float, _c_int, _c_void_p], _c_int),
     "fa2_fwd_varlen": ([_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
     "fa2_fwd_varlen_variant": ([_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_int, _c_void_p], _c_int),
+    "fa2_fwd_gqa": ([_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_void_p], _c_int),
+    "fa2_fwd_varlen_gqa": ([_c_void_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p], _c_int),
     "fa2_num_variants": ([_c_int], _c_int),
     "fa2_fwd_geometry": ([_c_int] * 6 + [ctypes.POINTER(_c_int)] * 4, _c_int),
     "fa2_status_str": ([_c_int], ctypes.c_char_p),
@@ -180,5 +182,74 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale
         st = lib.fa2_fwd_varlen_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                         cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, d,
                                         int(bool(causal)), float(scale), int(variant), _stream_ptr(q.device))
+    _check(st)
+    return out, lse
+
+
+def fwd_gqa(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, variant: int = 0):
+    """Grouped-/multi-query forward: q bf16 [B, H, N, d]; k, v bf16 [B, H_kv, N, d].
+
+    Query head h attends with key/value head h // (H // H_kv); H_kv must divide H.
+    Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N]).
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    if k.shape != v.shape:
+        raise ValueError(f"k, v shapes differ: {tuple(k.shape)} {tuple(v.shape)}")
+    B, H, N, d = q.shape
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d):
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    H_kv = k.shape[1]
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor("out", out, torch.bfloat16, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    if out.shape != q.shape or tuple(lse.shape) != (B, H, N) or out.device != q.device or lse.device != q.device:
+        raise ValueError("out/lse shape or device mismatch")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             B, H, H_kv, N, d, int(bool(causal)), float(scale), int(variant),
+                             _stream_ptr(q.device))
+    _check(st)
+    return out, lse
+
+
+def fwd_varlen_gqa(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
+                   out=None, lse=None, variant: int = 0):
+    """Packed variable-length grouped-query forward: q [H, T, d], k/v [H_kv, T, d] bf16."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, 3)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k/v shapes do not match q")
+    H, T, d = q.shape
+    H_kv = k.shape[0]
+    num_seqs = cu_seqlens.numel() - 1
+    if num_seqs < 0:
+        raise ValueError("cu_seqlens must have at least one entry")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_tensor("out", out, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    if out.shape != q.shape or tuple(lse.shape) != (H, T):
+        raise ValueError("out/lse shape mismatch")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_fwd_varlen_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, H_kv, d,
+                                    int(bool(causal)), float(scale), int(variant), _stream_ptr(q.device))
     _check(st)
     return out, lse

@@ -75,7 +75,9 @@ struct Params {
   float* lse;
   const int* cu_seqlens;  // varlen only
   int nb;                 // batch size, or number of sequences (varlen)
-  int H;
+  int H;                  // query heads
+  int Hkv;                // key/value heads (H for MHA)
+  int g;                  // query heads per key/value head, H / Hkv
   int N;                  // sequence length, or max_seqlen (varlen)
   int T;                  // tokens per head plane: N, or total_tokens (varlen)
   int tr;                 // row blocks per (batch|sequence, head)
@@ -203,7 +205,11 @@ void fa2_fwd_kernel(Params p) {
   const int bi = bh / p.H;
   const int h = bh - bi * p.H;
   int seq_len;
-  size_t row0;  // index of this sequence's first token in the [.., T, D] arrays
+  // Grouped/multi-query attention: query head h reads key/value head h / g, so the g query
+  // heads of a group share one K/V plane without copies.
+  const int hk = h / p.g;
+  size_t row0;    // index of this sequence's first token in the Q/O/LSE [.., T, D] arrays
+  size_t kvrow0;  // the same token in the K/V arrays
   if (VARLEN) {
     int a = p.cu_seqlens[bi];
     int e = p.cu_seqlens[bi + 1];
@@ -211,16 +217,18 @@ void fa2_fwd_kernel(Params p) {
     e = min(max(e, a), p.T);
     seq_len = e - a;
     row0 = (size_t)h * (size_t)p.T + (size_t)a;
+    kvrow0 = (size_t)hk * (size_t)p.T + (size_t)a;
   } else {
     seq_len = p.N;
     row0 = (size_t)bh * (size_t)p.N;
+    kvrow0 = ((size_t)bi * (size_t)p.Hkv + (size_t)hk) * (size_t)p.N;
   }
   const int q0 = i * TL::BR;
   if (q0 >= seq_len) return;  // uniform over the workgroup (varlen rows past the end)
 
   const uint16_t* __restrict__ qh = p.q + row0 * D;
-  const unsigned char* kh = (const unsigned char*)(p.k + row0 * D);
-  const unsigned char* vh = (const unsigned char*)(p.v + row0 * D);
+  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
+  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
 
   // Key tiles to visit: causal stops after the tile holding this block's last query.
   const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
@@ -535,7 +543,8 @@ void fa2_fwd_kernel_pp(Params p) {
   const int bi = bh / p.H;
   const int h = bh - bi * p.H;
   int seq_len;
-  size_t row0;
+  const int hk = h / p.g;
+  size_t row0, kvrow0;
   if (VARLEN) {
     int a = p.cu_seqlens[bi];
     int e = p.cu_seqlens[bi + 1];
@@ -543,16 +552,18 @@ void fa2_fwd_kernel_pp(Params p) {
     e = min(max(e, a), p.T);
     seq_len = e - a;
     row0 = (size_t)h * (size_t)p.T + (size_t)a;
+    kvrow0 = (size_t)hk * (size_t)p.T + (size_t)a;
   } else {
     seq_len = p.N;
     row0 = (size_t)bh * (size_t)p.N;
+    kvrow0 = ((size_t)bi * (size_t)p.Hkv + (size_t)hk) * (size_t)p.N;
   }
   const int q0 = i * TL::BR;
   if (q0 >= seq_len) return;
 
   const uint16_t* __restrict__ qh = p.q + row0 * D;
-  const unsigned char* kh = (const unsigned char*)(p.k + row0 * D);
-  const unsigned char* vh = (const unsigned char*)(p.v + row0 * D);
+  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
+  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
   const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
   const int nt = (kv_end + BC - 1) / BC;
 
@@ -943,9 +954,9 @@ int fa2_fwd_geometry(int B, int H, int N, int d, int causal, int variant, int* n
   return FA2_OK;
 }
 
-int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                    int H, int N, int d, int causal, float scale, int variant, void* stream) {
-  if (B <= 0 || H <= 0 || N < 0) return FA2_ERR_BAD_SHAPE;
+int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int H_kv, int N, int d, int causal, float scale, int variant, void* stream) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N < 0) return FA2_ERR_BAD_SHAPE;
   if (N == 0) return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   const Variant* var = nullptr;
   int st = check_common(q, k, v, o, lse, d, scale, variant, &var);
@@ -964,6 +975,8 @@ int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float*
   p.cu_seqlens = nullptr;
   p.nb = B;
   p.H = H;
+  p.Hkv = H_kv;
+  p.g = H / H_kv;
   p.N = N;
   p.T = N;
   p.tr = (int)tr;
@@ -972,16 +985,23 @@ int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float*
   return launch(*var, false, causal != 0, p, (int)wg, stream);
 }
 
-int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-            int N, int d, int causal, float scale, void* stream) {
-  return fa2_fwd_variant(q, k, v, o, lse, B, H, N, d, causal, scale, 0, stream);
+int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int d, int causal, float scale, int variant, void* stream) {
+  return fa2_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, variant, stream);
 }
 
-int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o, float* lse,
-                           const int* cu_seqlens, int num_seqs, int max_seqlen,
-                           int total_tokens, int H, int d, int causal, float scale, int variant,
-                           void* stream) {
-  if (H <= 0 || num_seqs < 0 || max_seqlen < 0 || total_tokens < 0) return FA2_ERR_BAD_SHAPE;
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+            int N, int d, int causal, float scale, void* stream) {
+  return fa2_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, 0, stream);
+}
+
+int fa2_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                       int H, int H_kv, int d, int causal, float scale, int variant,
+                       void* stream) {
+  if (H <= 0 || H_kv <= 0 || H % H_kv != 0 || num_seqs < 0 || max_seqlen < 0 ||
+      total_tokens < 0)
+    return FA2_ERR_BAD_SHAPE;
   if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
     return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   if (!cu_seqlens) return FA2_ERR_NULL_PTR;
@@ -1002,6 +1022,8 @@ int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o,
   p.cu_seqlens = cu_seqlens;
   p.nb = num_seqs;
   p.H = H;
+  p.Hkv = H_kv;
+  p.g = H / H_kv;
   p.N = max_seqlen;
   p.T = total_tokens;
   p.tr = (int)tr;
@@ -1010,11 +1032,19 @@ int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o,
   return launch(*var, true, causal != 0, p, (int)wg, stream);
 }
 
+int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const int* cu_seqlens, int num_seqs, int max_seqlen,
+                           int total_tokens, int H, int d, int causal, float scale, int variant,
+                           void* stream) {
+  return fa2_fwd_varlen_gqa(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens, H,
+                            H, d, causal, scale, variant, stream);
+}
+
 int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                    const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens, int H,
                    int d, int causal, float scale, void* stream) {
-  return fa2_fwd_varlen_variant(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen,
-                                total_tokens, H, d, causal, scale, 0, stream);
+  return fa2_fwd_varlen_gqa(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens, H,
+                            H, d, causal, scale, 0, stream);
 }
 
 }  // extern "C"

@@ -44,7 +44,7 @@ extern "C" {
 enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULL_PTR = 1,            /* a required pointer is NULL */
-  FA2_ERR_BAD_SHAPE = 2,           /* B or H <= 0, N < 0, or inconsistent varlen sizes */
+  FA2_ERR_BAD_SHAPE = 2,           /* B, H or H_kv <= 0, H_kv not dividing H, N < 0, ... */
   FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* d is not 64 or 128 */
   FA2_ERR_MISALIGNED = 4,          /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
   FA2_ERR_BAD_SCALE = 5,           /* scale is NaN or infinite */
@@ -96,6 +96,27 @@ int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o,
                            const int* cu_seqlens, int num_seqs, int max_seqlen,
                            int total_tokens, int H, int d, int causal, float scale,
                            int variant, void* stream);
+
+/*
+ * Grouped-query and multi-query forward: H query heads share H_kv key/value heads, query
+ * head h reading key/value head floor(h / g) with g = H / H_kv, and no copy of K or V is
+ * made ("FlashAttention 2: ..." reading notes, papers.chlience.com, section 5.6, the head
+ * index mapping for MQA/GQA; paper-graph-ui summary, section 3.4, "The Backward Pass:
+ * Simpler Statistics, Same Structure", its paragraph on multi-query and grouped-query
+ * attention).
+ *   q, o : bf16 [B, H, N, d];  k, v : bf16 [B, H_kv, N, d];  lse : fp32 [B, H, N].
+ *   varlen: q, o [H, total_tokens, d]; k, v [H_kv, total_tokens, d]; lse [H, total_tokens].
+ *   H_kv must divide H (else FA2_ERR_BAD_SHAPE); H_kv == H is ordinary multi-head attention
+ *   and H_kv == 1 is multi-query attention. variant as for fa2_fwd_variant (0 = default).
+ * Everything else (validation, ownership, asynchrony, zero-size calls) is as for fa2_fwd.
+ */
+int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int H_kv, int N, int d, int causal, float scale, int variant,
+                void* stream);
+int fa2_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                       int H, int H_kv, int d, int causal, float scale, int variant,
+                       void* stream);
 
 /* Number of kernel variants for head dimension d (0 if d is unsupported). Host only. */
 int fa2_num_variants(int d);

@@ -3,6 +3,8 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may import this package. The product path never does.
 """
-from .attention import attention, attention_head, attention_rows, attention_varlen
+from .attention import (attention, attention_gqa, attention_head, attention_rows, attention_varlen,
+                        attention_varlen_gqa, kv_head)
 
-__all__ = ["attention", "attention_head", "attention_rows", "attention_varlen"]
+__all__ = ["attention", "attention_gqa", "attention_head", "attention_rows", "attention_varlen",
+           "attention_varlen_gqa", "kv_head"]

@@ -30,6 +30,9 @@ Sources for each line:
     paper-graph-ui §3.4, "Tweak 2: Store Logsumexp".
   * causal: entries with column index greater than row index are -inf:
     paper-graph-ui §3.4, "Causal masking optimization"; chlience notes §5.6.
+  * grouped/multi-query attention: query head h uses key/value head
+    floor(h / g), g = H_q / H_kv query heads per key/value head, K and V never
+    copied: chlience notes §5.6 (the MQA/GQA head index mapping).
 
 Readings where the pages are silent:
   * the scale multiplies Q K^T before the softmax, and LSE is taken over the
@@ -46,7 +49,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attention", "attention_head", "attention_rows", "attention_varlen"]
+__all__ = ["attention", "attention_gqa", "attention_head", "attention_rows", "attention_varlen",
+           "attention_varlen_gqa", "kv_head"]
 
 
 def _as_f64(x) -> np.ndarray:
@@ -135,4 +139,46 @@ def attention_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
         a, b = cu[s], cu[s + 1]
         for h in range(H):
             o[h, a:b], lse[h, a:b] = attention_head(q[h, a:b], k[h, a:b], v[h, a:b], causal, scale)
+    return o, lse
+
+
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """Key/value head read by query head h: floor(h / g) with g = H / H_kv (chlience §5.6)."""
+    if H_kv <= 0 or H % H_kv:
+        raise ValueError(f"H_kv={H_kv} must divide H={H}")
+    return h // (H // H_kv)
+
+
+def attention_gqa(q, k, v, causal: bool, scale: float):
+    """Grouped-query attention: q [B, H, N, d]; k, v [B, H_kv, N, d] with H_kv | H.
+
+    Each query head is the plain definition (``attention_head``) against the
+    key/value head ``kv_head`` maps it to. Returns (O [B,H,N,d], LSE [B,H,N]).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, _ = q.shape
+    H_kv = k.shape[1]
+    o = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, hk], v[b, hk], causal, scale)
+    return o, lse
+
+
+def attention_varlen_gqa(q, k, v, cu_seqlens, causal: bool, scale: float):
+    """Packed grouped-query attention: q [H, T, d]; k, v [H_kv, T, d]; sequences as in
+    ``attention_varlen``. Returns (O [H, T, d], LSE [H, T])."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    H, T, _ = q.shape
+    H_kv = k.shape[0]
+    o = np.zeros(q.shape[:2] + (v.shape[2],))
+    lse = np.zeros((H, T))
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            o[h, a:b], lse[h, a:b] = attention_head(q[h, a:b], k[hk, a:b], v[hk, a:b], causal, scale)
     return o, lse

@@ -81,13 +81,14 @@ def _randn_bf16(shape, gen: torch.Generator, mult: float = 1.0) -> torch.Tensor:
     return x.to(torch.bfloat16)
 
 
-def make_qkv(B: int, H: int, N: int, d: int, seed: int, k_scale: float = 1.0):
-    """Return CPU bf16 tensors q, k, v of shape [B, H, N, d] (drawn in that order)."""
+def make_qkv(B: int, H: int, N: int, d: int, seed: int, k_scale: float = 1.0, H_kv: int | None = None):
+    """Return CPU bf16 tensors q [B, H, N, d] and k, v [B, H_kv, N, d] (drawn in that
+    order; H_kv defaults to H)."""
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
-    shape = (B, H, N, d)
-    q = _randn_bf16(shape, gen)
-    k = _randn_bf16(shape, gen, k_scale)
-    v = _randn_bf16(shape, gen)
+    H_kv = H if H_kv is None else int(H_kv)
+    q = _randn_bf16((B, H, N, d), gen)
+    k = _randn_bf16((B, H_kv, N, d), gen, k_scale)
+    v = _randn_bf16((B, H_kv, N, d), gen)
     return q, k, v
 
 
@@ -97,10 +98,11 @@ def varlen_lengths(num_seqs: int, min_len: int, max_len: int, gen: torch.Generat
 
 
 def make_varlen(H: int, d: int, seed: int, lengths=None, num_seqs: int = 16,
-                min_len: int = 128, max_len: int = 4096, k_scale: float = 1.0):
+                min_len: int = 128, max_len: int = 4096, k_scale: float = 1.0, H_kv: int | None = None):
     """Packed variable-length batch.
 
-    Returns (q, k, v, cu_seqlens, lengths): q, k, v are CPU bf16 [H, T, d],
+    Returns (q, k, v, cu_seqlens, lengths): q is CPU bf16 [H, T, d], k and v
+    [H_kv, T, d] (H_kv defaults to H),
     cu_seqlens is an int32 CPU tensor [num_seqs + 1] with cu[0] = 0 and
     cu[s+1] - cu[s] = lengths[s]. If ``lengths`` is None it is drawn first from
     the same generator, then q, k, v are drawn in that order.
@@ -110,10 +112,10 @@ def make_varlen(H: int, d: int, seed: int, lengths=None, num_seqs: int = 16,
         lengths = varlen_lengths(num_seqs, min_len, max_len, gen)
     lengths = [int(x) for x in lengths]
     T = sum(lengths)
-    shape = (H, T, d)
-    q = _randn_bf16(shape, gen)
-    k = _randn_bf16(shape, gen, k_scale)
-    v = _randn_bf16(shape, gen)
+    H_kv = H if H_kv is None else int(H_kv)
+    q = _randn_bf16((H, T, d), gen)
+    k = _randn_bf16((H_kv, T, d), gen, k_scale)
+    v = _randn_bf16((H_kv, T, d), gen)
     cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
     if lengths:
         cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)

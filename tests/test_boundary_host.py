@@ -136,6 +136,38 @@ def test_varlen_empty_is_ok():
     assert _varlen(T=0, q=None, k=None, v=None, o=None, lse=None) == 0
 
 
+def _gqa(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=8, H_kv=2, N=16, d=128, causal=1, scale=0.125,
+         variant=0):
+    return fa2.load_library().fa2_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, variant, None)
+
+
+def _varlen_gqa(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, S=2, maxlen=16, T=32, H=8, H_kv=4, d=64,
+                causal=1, scale=0.125, variant=0):
+    return fa2.load_library().fa2_fwd_varlen_gqa(q, k, v, o, lse, cu, S, maxlen, T, H, H_kv, d, causal, scale,
+                                                 variant, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(H_kv=0), 2), (dict(H_kv=-2), 2), (dict(H_kv=3), 2), (dict(H_kv=16), 2), (dict(H=0), 2),
+    (dict(k=None), 1), (dict(v=FAKE + 4), 4), (dict(d=32), 3), (dict(variant=77), 8),
+    (dict(scale=float("nan")), 5),
+])
+def test_gqa_validation(kwargs, code):
+    assert _gqa(**kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(H_kv=0), 2), (dict(H_kv=3), 2), (dict(cu=None), 1), (dict(d=96), 3), (dict(variant=-1), 8),
+])
+def test_varlen_gqa_validation(kwargs, code):
+    assert _varlen_gqa(**kwargs) == code
+
+
+def test_gqa_empty_is_ok():
+    assert _gqa(q=None, k=None, v=None, o=None, lse=None, N=0) == 0
+    assert _varlen_gqa(T=0, q=None, k=None, v=None, o=None, lse=None) == 0
+
+
 def _gpu_present():
     if os.path.exists("/dev/kfd"):
         return True
@@ -151,6 +183,8 @@ def test_no_device_reported():
     # Valid arguments: validation passes, then the device query fails before any launch.
     assert _fwd() == 6
     assert _varlen() == 6
+    assert _gqa() == 6
+    assert _varlen_gqa() == 6
 
 
 def test_binding_rejects_cpu_tensors():
@@ -158,6 +192,8 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa2.fwd(q, q, q)
+    with pytest.raises(ValueError):
+        fa2.fwd_gqa(q, q, q)
 
 
 def test_metric_flops():

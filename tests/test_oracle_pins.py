@@ -30,7 +30,8 @@ import pytest
 import scipy.special
 import torch
 
-from oracle import attention, attention_head, attention_rows, attention_varlen
+from oracle import (attention, attention_gqa, attention_head, attention_rows, attention_varlen,
+                    attention_varlen_gqa, kv_head)
 
 RNG = np.random.default_rng(12345)
 
@@ -434,3 +435,92 @@ def test_empty_inputs():
     assert o.shape == (0, 4) and l.shape == (0,)
     o, l = attention_varlen(np.zeros((2, 0, 4)), np.zeros((2, 0, 4)), np.zeros((2, 0, 4)), [0], True, 1.0)
     assert o.shape == (2, 0, 4) and l.shape == (2, 0)
+
+
+# ---------------------------------------------------------------------------
+# Grouped/multi-query attention (chlience notes §5.6: query head h reads
+# key/value head floor(h / g), g = H / H_kv, without copying K or V).
+# ---------------------------------------------------------------------------
+
+def _gqa_brute(q, k, v, causal, scale):
+    """Brute force over [B, H, N, d] with the group written as a contiguous block of
+    H / H_kv query heads per key/value head: head h is in group h * H_kv // H."""
+    B, H = q.shape[:2]
+    H_kv = k.shape[1]
+    o = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.zeros(q.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            grp = (h * H_kv) // H
+            o[b, h], lse[b, h] = _brute_force(q[b, h].tolist(), k[b, grp].tolist(), v[b, grp].tolist(),
+                                              causal, scale)
+    return o, lse
+
+
+def pin_gqa_brute_force(impl):
+    rng = np.random.default_rng(31)
+    for H, H_kv in ((6, 1), (6, 2), (6, 3), (6, 6), (4, 2)):
+        for causal in (False, True):
+            q = rng.standard_normal((2, H, 5, 3))
+            k = rng.standard_normal((2, H_kv, 5, 3))
+            v = rng.standard_normal((2, H_kv, 5, 3))
+            o_ref, l_ref = _gqa_brute(q, k, v, causal, 0.6)
+            o, l = impl(q, k, v, causal, 0.6)
+            if not (np.allclose(o, o_ref, atol=1e-12) and np.allclose(l, l_ref, atol=1e-12)):
+                return f"gqa brute force mismatch H={H} H_kv={H_kv} causal={causal}"
+    return None
+
+
+def test_gqa_oracle_pinned():
+    assert pin_gqa_brute_force(attention_gqa) is None
+
+
+def test_gqa_pin_catches_interleaved_mapping():
+    """Planted mistake: h % H_kv (interleaved groups) instead of floor(h / g)."""
+    def interleaved(q, k, v, causal, scale):
+        k2 = np.stack([k[:, h % k.shape[1]] for h in range(q.shape[1])], axis=1)
+        v2 = np.stack([v[:, h % v.shape[1]] for h in range(q.shape[1])], axis=1)
+        return attention(q, k2, v2, causal, scale)
+    assert pin_gqa_brute_force(interleaved) is not None
+
+
+def test_gqa_closed_forms():
+    rng = np.random.default_rng(32)
+    # H_kv == H is multi-head attention.
+    q, k, v = (rng.standard_normal((1, 4, 7, 5)) for _ in range(3))
+    o1, l1 = attention_gqa(q, k, v, True, 0.4)
+    o2, l2 = attention(q, k, v, True, 0.4)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # Multi-query: every query head with the same q gives the same row; heads with
+    # different q differ.
+    qh = rng.standard_normal((7, 5))
+    q = np.stack([qh, qh, rng.standard_normal((7, 5))])[None]
+    k, v = rng.standard_normal((1, 1, 7, 5)), rng.standard_normal((1, 1, 7, 5))
+    o, l = attention_gqa(q, k, v, False, 0.5)
+    assert np.array_equal(o[0, 0], o[0, 1]) and not np.allclose(o[0, 0], o[0, 2])
+    # Identical V rows inside each group: O of every head of group j equals that row.
+    vrow = rng.standard_normal((2, 5))
+    v = np.broadcast_to(vrow[None, :, None, :], (1, 2, 7, 5)).copy()
+    q, k = rng.standard_normal((1, 6, 7, 5)), rng.standard_normal((1, 2, 7, 5))
+    o, _ = attention_gqa(q, k, v, True, 0.5)
+    for h in range(6):
+        assert np.allclose(o[0, h], vrow[h // 3], atol=1e-14)
+    with pytest.raises(ValueError):
+        kv_head(0, 6, 4)
+
+
+def test_varlen_gqa_matches_brute_force():
+    rng = np.random.default_rng(33)
+    lengths = [3, 1, 6]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, H_kv, d = int(cu[-1]), 4, 2, 3
+    q = rng.standard_normal((H, T, d))
+    k, v = rng.standard_normal((H_kv, T, d)), rng.standard_normal((H_kv, T, d))
+    for causal in (False, True):
+        o, l = attention_varlen_gqa(q, k, v, cu, causal, 0.7)
+        for s in range(len(lengths)):
+            a, b = cu[s], cu[s + 1]
+            for h in range(H):
+                grp = h * H_kv // H
+                ob, lb = _brute_force(q[h, a:b].tolist(), k[grp, a:b].tolist(), v[grp, a:b].tolist(), causal, 0.7)
+                assert np.allclose(o[h, a:b], ob, atol=1e-12) and np.allclose(l[h, a:b], lb, atol=1e-12)
