@@ -57,6 +57,14 @@ def algorithmic_bytes(w, lengths=None, kv_heads=None) -> int:
     return 4 * w.B * (w.H + hk) * w.N * w.d + 4 * w.B * w.H * w.N
 
 
+def bwd_algorithmic_bytes(w, kv_heads=None) -> int:
+    """Backward: read Q, K, V, O, dO and LSE once, write dQ, dK, dV once (bf16); D is
+    written and read once (fp32)."""
+    hk = w.H if kv_heads is None else kv_heads
+    rows_q, rows_kv = w.B * w.H * w.N, w.B * hk * w.N
+    return 2 * w.d * (4 * rows_q + 4 * rows_kv) + 4 * rows_q + 8 * rows_q
+
+
 def load_traffic():
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -131,6 +139,22 @@ def run(args):
         def step():
             fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, variant=args.variant)
 
+    if args.bwd:
+        if w.varlen:
+            raise SystemExit("--bwd runs on fixed-length workloads")
+        gen = torch.Generator(device="cpu").manual_seed(1000 + w.seed)
+        dod = torch.randn(qd.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).to(dev)
+        if kd.shape[1] == qd.shape[1]:
+            fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        else:
+            fa2.fwd_gqa(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        delta = torch.empty_like(lse)
+        flops = 2.5 * flops   # five matrix products against the forward's two
+
+        def step():
+            fa2.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+
     if args.calib_copy:   # a plain copy kernel of known size, for counter calibration
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -154,7 +178,7 @@ def run(args):
     tflops = flops / (ms * 1e-3) / 1e12
 
     traffic = None
-    t = load_traffic() if (w.name == "c4" and not args.kv_heads and args.variant == 0) else None
+    t = load_traffic() if (w.name == "c4" and not args.kv_heads and args.variant == 0 and not args.bwd) else None
     if t is not None:
         traffic = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
@@ -166,8 +190,11 @@ def run(args):
     if args.kv_heads:
         config.update({"workload": f"{w.name} with grouped-query K/V: {w.description}, "
                                    f"{args.kv_heads} key/value heads", "H_kv": args.kv_heads})
+    if args.bwd:
+        config.update({"workload": f"backward of {config['workload']}", "kernel_variant": "bwd_dq+bwd_dkdv"})
     out = {
-        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak",
+        "metric": ("attention bwd TFLOP/s (2.5 x 4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak" if args.bwd
+                   else "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -177,7 +204,7 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3)
-                        if w.name == "c4" and not args.kv_heads else None),
+                        if w.name == "c4" and not (args.kv_heads or args.bwd) else None),
         "dtype": "bf16",
         "data": "synthetic",
         "config": config,
@@ -189,14 +216,15 @@ def run(args):
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": algorithmic_bytes(w, lengths, args.kv_heads or None),
+            "algorithmic_bytes": (bwd_algorithmic_bytes(w, args.kv_heads or None) if args.bwd
+                                  else algorithmic_bytes(w, lengths, args.kv_heads or None)),
             "flops_per_launch": flops,
             "kernel_ms": round(ms, 5),
         },
     }
     if args.cpu_baseline_heads > 0:
         out["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_baseline_heads)
-                               if not (w.varlen or args.kv_heads) else None)
+                               if not (w.varlen or args.kv_heads or args.bwd) else None)
     print(json.dumps(out), flush=True)
 
 
@@ -239,6 +267,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward (dQ, dK, dV from dO, O, LSE) instead of the forward")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped-query attention: K/V with this many heads (must divide H; 0: H)")
     ap.add_argument("--cpu-baseline-heads", type=int, default=8,

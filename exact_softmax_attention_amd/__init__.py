@@ -1,4 +1,4 @@
-"""Exact softmax attention forward (FlashAttention-2 style) on AMD MI355X (gfx950).
+"""Exact softmax attention, forward and backward (FlashAttention-2 style), on AMD MI355X (gfx950).
 
 Thin ctypes binding over libfa2.so, whose C ABI is declared in include/fa2.h. This module
 only marshals arguments: it checks tensor metadata, allocates outputs with torch, passes
@@ -11,6 +11,8 @@ from ._lib import (
     FA2_ABI_VERSION,
     Fa2Error,
     STATUS,
+    bwd,
+    bwd_varlen,
     fwd,
     fwd_gqa,
     fwd_varlen,
@@ -26,6 +28,8 @@ __all__ = [
     "FA2_ABI_VERSION",
     "Fa2Error",
     "STATUS",
+    "bwd",
+    "bwd_varlen",
     "fwd",
     "fwd_gqa",
     "fwd_varlen",

@@ -32,6 +32,8 @@ _SIGNATURES = {
     "fa2_fwd_varlen_variant": ([_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_int, _c_void_p], _c_int),
     "fa2_fwd_gqa": ([_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_void_p], _c_int),
     "fa2_fwd_varlen_gqa": ([_c_void_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p], _c_int),
+    "fa2_bwd": ([_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
+    "fa2_bwd_varlen": ([_c_void_p] * 11 + [_c_int] * 7 + [_c_float, _c_void_p], _c_int),
     "fa2_num_variants": ([_c_int], _c_int),
     "fa2_fwd_geometry": ([_c_int] * 6 + [ctypes.POINTER(_c_int)] * 4, _c_int),
     "fa2_status_str": ([_c_int], ctypes.c_char_p),
@@ -253,3 +255,81 @@ def fwd_varlen_gqa(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, s
                                     int(bool(causal)), float(scale), int(variant), _stream_ptr(q.device))
     _check(st)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None, delta=None):
+    """Gradients (dq, dk, dv) of the forward for upstream gradient ``dout``.
+
+    q, o, dout: bf16 [B, H, N, d]; k, v: bf16 [B, H_kv, N, d] (H_kv divides H); lse: fp32
+    [B, H, N] from the forward with the same ``scale``. ``delta`` (fp32 [B, H, N]) is the
+    scratch buffer for D = rowsum(dout * o); outputs and scratch are allocated when not given.
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or \
+            (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d) or tuple(lse.shape) != (B, H, N):
+        raise ValueError("q/o/dout [B,H,N,d], k/v [B,H_kv,N,d], lse [B,H,N] shapes do not match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(ref.shape)}")
+    _check_tensor("delta", delta, torch.float32, 3)
+    if tuple(delta.shape) != (B, H, N):
+        raise ValueError("delta must be [B, H, N]")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                         B, H, H_kv, N, d, int(bool(causal)), float(scale), _stream_ptr(q.device))
+    _check(st)
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool = False,
+               scale: float | None = None, dq=None, dk=None, dv=None, delta=None):
+    """Packed variable-length backward: q, o, dout [H, T, d]; k, v [H_kv, T, d]; lse [H, T]."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    H, T, d = q.shape
+    H_kv = k.shape[0]
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or k.shape[1:] != q.shape[1:] \
+            or tuple(lse.shape) != (H, T):
+        raise ValueError("q/o/dout [H,T,d], k/v [H_kv,T,d], lse [H,T] shapes do not match")
+    num_seqs = cu_seqlens.numel() - 1
+    if num_seqs < 0:
+        raise ValueError("cu_seqlens must have at least one entry")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((H, T), dtype=torch.float32, device=q.device) if delta is None else delta
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, torch.bfloat16, 3)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(ref.shape)}")
+    _check_tensor("delta", delta, torch.float32, 2)
+    if tuple(delta.shape) != (H, T):
+        raise ValueError("delta must be [H, T]")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                                cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, H_kv, d,
+                                int(bool(causal)), float(scale), _stream_ptr(q.device))
+    _check(st)
+    return dq, dk, dv

@@ -13,7 +13,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "fa2_fwd.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", "fa2_fwd.hip"), os.path.join(PKG_DIR, "csrc", "fa2_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libfa2.so")
 ARCH = "gfx950"
@@ -39,7 +39,7 @@ def compile_flags() -> list[str]:
 def build(verbose: bool = True, extra_flags: list[str] | None = None, out: str = LIB) -> str:
     """Compile the HIP sources into ``out`` (always recompiles). Returns the path."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *(extra_flags or []), SRC, "-o", tmp]
+    cmd = [hipcc(), *compile_flags(), *(extra_flags or []), *SRCS, "-o", tmp]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

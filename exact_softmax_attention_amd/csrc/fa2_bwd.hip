@@ -1,0 +1,737 @@
+// fa2_bwd.hip — gfx950 (CDNA4) backward kernels for exact softmax attention, and their C ABI
+// (declared in include/fa2.h).
+//
+// Page abbreviations used below:
+//   [CHL] "FlashAttention 2: Faster Attention with Better Parallelism and Work Partitioning",
+//         reading notes at papers.chlience.com
+//   [PGU] "FlashAttention-2: Faster Attention with Better Parallelism and Work Partitioning",
+//         paper-graph-ui summary
+//
+// The backward of O = softmax(scale·QK^T) V, given dO, the forward's O and its logsumexp L,
+// recomputes the probabilities from L instead of storing them ([CHL] 5.2, 5.3; [PGU] 3.4,
+// "The Backward Pass: Simpler Statistics, Same Structure"):
+//     P   = exp(scale·QK^T - L)            (0 where the causal mask removes a key)
+//     D   = rowsum(dO ∘ O)
+//     dV  = P^T dO
+//     dP  = dO V^T
+//     dS  = P ∘ (dP - D)
+//     dQ  = scale · dS K
+//     dK  = scale · dS^T Q
+// (the pages write dQ = dS K and dK = dS^T Q for an unscaled score; with S = scale·QK^T the
+// chain rule adds the factor scale). Grouped-query attention sums dK and dV over the query
+// heads that share a key/value head ([CHL] 5.6).
+//
+// Work split. The pages' single kernel walks key/value column blocks in the outer loop and
+// merges dQ across column blocks with atomic adds in HBM ([CHL] 5.4; [PGU] 3.4, "Backward
+// pass parallelization"). Here the work is split over two kernels instead, which needs no
+// atomics and gives bitwise-reproducible gradients:
+//   fa2_bwd_dq_kernel    rows outer (one workgroup = 128 query rows, 32 per wave), key/value
+//                        tiles inner: S, dP, dS, then dQ += dS K. It also writes D.
+//   fa2_bwd_dkdv_kernel  columns outer (one workgroup = 128 keys of one key/value head, 32 per
+//                        wave), query tiles of every query head of the group inner: S, dP,
+//                        dS, then dV += P^T dO and dK += dS^T Q.
+// S and dP are computed in both (7 matrix products instead of the pages' 5).
+//
+// Layouts. The dQ kernel computes S^T = K Q^T and dP^T = V dO^T so that a lane owns one query
+// (its statistics L and D are per lane), exactly as the forward. The dK/dV kernel computes
+// S = Q K^T and dP = dO V^T so that a lane owns one key; P and dS then sit in registers in the
+// B-operand layout of dV^T = dO^T P and dK^T = Q^T dS, whose A operands (dO^T, Q^T) are
+// gathered from row-major tiles in LDS by transposed reads. Tiles that are read both by rows
+// and transposed use a swizzle that keeps both read patterns free of bank conflicts.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa2.h"
+#include "fa2_dev.h"
+
+namespace {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;           // D = rowsum(dO ∘ O), fp32, laid out like lse
+  const int* cu_seqlens;  // varlen only
+  int nb;                 // batch size, or number of sequences (varlen)
+  int H;                  // query heads
+  int Hkv;                // key/value heads
+  int g;                  // H / Hkv
+  int N;                  // sequence length, or max_seqlen (varlen)
+  int T;                  // tokens per head plane: N, or total_tokens (varlen)
+  int nblk;               // 128-row (dQ) or 128-key (dK/dV) blocks per sequence
+  int heads_per_xcd;      // > 0: XCD-aware workgroup order
+  float c;                // |scale| * log2(e), at least 1e-30
+  float scale;            // the signed softmax scale
+  uint32_t qflip;         // 0x80008000 negates Q in the score products (scale < 0), else 0
+};
+
+// Row swizzle of a bf16 tile in LDS (16-byte chunk index XOR per row), chosen so that both
+// access patterns used on one tile are free of bank conflicts: 16-byte row reads by 16
+// consecutive rows at one logical chunk, and transposed 8-byte reads of 4 consecutive rows
+// (starting at a multiple of 4) by 4 consecutive chunks. Period 16 in the row index.
+template <int D>
+__device__ __forceinline__ int dswz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Workgroup id -> (pair index in [0, npairs), block index). As in the forward: workgroup id
+// goes to XCD id % 8 and, when npairs % 8 == 0, each XCD owns a contiguous set of pairs.
+// Causal launches start with the heaviest blocks: HEAVY_HIGH puts the largest block index
+// first (query blocks of the dQ kernel), otherwise the smallest (key blocks of dK/dV).
+template <bool CAUSAL, bool HEAVY_HIGH>
+__device__ __forceinline__ void decode_bwd(int npairs, int nblk, int hpx, int& pair, int& blk) {
+  const int id = blockIdx.x;
+  if (hpx > 0) {
+    const int x = id & 7, slot = id >> 3;
+    int hl;
+    if (CAUSAL) {
+      const int r = slot / hpx;
+      blk = HEAVY_HIGH ? nblk - 1 - r : r;
+      hl = slot - r * hpx;
+    } else {
+      hl = slot / nblk;
+      blk = slot - hl * nblk;
+    }
+    pair = x * hpx + hl;
+  } else {
+    const int r = id / npairs;
+    blk = (CAUSAL && !HEAVY_HIGH) ? r : nblk - 1 - r;
+    pair = id - r * npairs;
+  }
+}
+
+// Token range of sequence bi: [tok0, tok0 + len) of each head plane.
+template <bool VARLEN>
+__device__ __forceinline__ void seq_range(const BwdParams& p, int bi, int& tok0, int& len) {
+  if (VARLEN) {
+    int a = p.cu_seqlens[bi];
+    int e = p.cu_seqlens[bi + 1];
+    a = min(max(a, 0), p.T);
+    e = min(max(e, a), p.T);
+    tok0 = a;
+    len = e - a;
+  } else {
+    tok0 = 0;
+    len = p.N;
+  }
+}
+
+// First element (row index into [.., T, D] arrays) of the plane of query head h / key-value
+// head hk of batch (or sequence) bi.
+template <bool VARLEN>
+__device__ __forceinline__ size_t q_plane(const BwdParams& p, int bi, int h) {
+  return VARLEN ? (size_t)h * (size_t)p.T : ((size_t)bi * p.H + h) * (size_t)p.N;
+}
+template <bool VARLEN>
+__device__ __forceinline__ size_t kv_plane(const BwdParams& p, int bi, int hk) {
+  return VARLEN ? (size_t)hk * (size_t)p.T : ((size_t)bi * p.Hkv + hk) * (size_t)p.N;
+}
+
+// ---- dQ kernel -------------------------------------------------------------------------
+
+template <int D, int BC>
+struct DqTile {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BR = 32 * WAVES;
+  static constexpr int ROWB = 2 * D;
+  static constexpr int TILEB = BC * ROWB;           // one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;          // K tile then V tile
+  static constexpr int LDS_BYTES = 2 * STAGEB;
+  static constexpr int DMA_PER_WAVE = TILEB / 1024 / WAVES;
+  static constexpr int NKB = BC / 32;
+  static constexpr int NKC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int NPC = BC / 16;
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(BC % 32 == 0 && DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
+};
+
+template <int D, int BC, bool CAUSAL, bool VARLEN>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dq_kernel(BwdParams p) {
+  using TL = DqTile<D, BC>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  int bh, i;
+  decode_bwd<CAUSAL, true>(p.nb * p.H, p.nblk, p.heads_per_xcd, bh, i);
+  const int bi = bh / p.H;
+  const int h = bh - bi * p.H;
+  int tok0, seq_len;
+  seq_range<VARLEN>(p, bi, tok0, seq_len);
+  const int q0 = i * TL::BR;
+  if (q0 >= seq_len) return;
+  const size_t row0 = q_plane<VARLEN>(p, bi, h) + (size_t)tok0;
+  const size_t kvrow0 = kv_plane<VARLEN>(p, bi, h / p.g) + (size_t)tok0;
+  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
+  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
+  const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
+  const int nt = (kv_end + BC - 1) / BC;
+
+  // This lane's query: Q^T and dO^T as B fragments, L in base 2, and D = rowsum(dO ∘ O)
+  // (each 32-lane half holds 8 of every 16 head-dimension values).
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  const bool valid = qrow < seq_len;
+  bf16x8 qf[TL::NKC], df[TL::NKC];
+  float dot = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc) {
+    u32x4 tq = {0u, 0u, 0u, 0u}, td = tq, to = tq;
+    if (valid) {
+      const size_t off = (row0 + (size_t)qrow) * D + kc * 16 + hl * 8;
+      tq = *(const u32x4*)(p.q + off);
+      td = *(const u32x4*)(p.dout + off);
+      to = *(const u32x4*)(p.o + off);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dot += bf16_lo(td[e]) * bf16_lo(to[e]) + bf16_hi(td[e]) * bf16_hi(to[e]);
+    qf[kc] = as_bf16x8(tq ^ p.qflip);
+    df[kc] = as_bf16x8(td);
+  }
+  const float drow = halves_sum(dot);
+  const float l2 = valid ? p.lse[row0 + (size_t)qrow] * kLog2e : 0.f;
+  if (valid && hl == 0) p.delta[row0 + (size_t)qrow] = drow;
+
+  // K/V staging (direct global -> LDS), both tiles with the dual-pattern swizzle.
+  int drow_[TL::DMA_PER_WAVE];
+  uint32_t doff[TL::DMA_PER_WAVE];
+#pragma unroll
+  for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+    const int b = wave * TL::DMA_PER_WAVE + d;
+    const int o = b * 1024 + lane * 16;
+    const int r = o / TL::ROWB;
+    const int pch = (o % TL::ROWB) / 16;
+    drow_[d] = r;
+    doff[d] = r * TL::ROWB + ((pch ^ dswz<D>(r)) * 16);
+  }
+  auto dma_tile = [&](int j, unsigned char* stage) {
+    const int key0 = j * BC;
+    const unsigned char* kt = kh + (size_t)key0 * TL::ROWB;
+    const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
+    const uint32_t ks_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
+    const uint32_t vs_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
+    const int last = seq_len - 1 - key0;   // rows past the end re-read the last valid row
+#pragma unroll
+    for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+      const uint32_t back = (uint32_t)(drow_[d] - min(drow_[d], last)) * TL::ROWB;
+      dma16(kt, doff[d] - back, ks_a + d * 1024);
+      dma16(vt, doff[d] - back, vs_a + d * 1024);
+    }
+  };
+
+  // Row reads (A operands of S^T and dP^T): row kb*32 + l32, logical chunk 2kc + hl.
+  int raddr[TL::NKC];
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc)
+    raddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ dswz<D>(l32)) * 16);
+  // Transposed reads of K (A operand K^T of dQ^T): rows 16c + 4hl + (lane%16)/4 (low half of
+  // the fragment) and the same + 8 (high half), columns 32db + 16((lane/16)%2) + 4(lane%4).
+  const int tr0 = 4 * hl + ((lane & 15) >> 2);
+  int taddr_lo[TL::NDB], taddr_hi[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) {
+    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    taddr_lo[db] = tr0 * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0)) * 16) + (col & 7) * 2;
+    taddr_hi[db] = (tr0 + 8) * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0 + 8)) * 16) + (col & 7) * 2;
+  }
+
+  f32x16 dqacc[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) dqacc[db] = (f32x16){};
+
+  auto compute_tile = [&](int j, const unsigned char* stage) {
+    const int key0 = j * BC;
+    if ((CAUSAL && key0 > qw0 + 31) || qw0 >= seq_len) return;
+    f32x16 s[TL::NKB], dp[TL::NKB];
+#pragma unroll
+    for (int kb = 0; kb < TL::NKB; ++kb) {
+      s[kb] = (f32x16){};
+      dp[kb] = (f32x16){};
+#pragma unroll
+      for (int kc = 0; kc < TL::NKC; ++kc) {
+        const bf16x8 ka = *(const bf16x8*)(stage + kb * 32 * TL::ROWB + raddr[kc]);
+        const bf16x8 va = *(const bf16x8*)(stage + TL::TILEB + kb * 32 * TL::ROWB + raddr[kc]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kc], dp[kb], 0, 0, 0);
+      }
+    }
+    // Causal and ragged masks (key > query, key >= length), as in the forward.
+    if ((CAUSAL && key0 + BC - 1 > qw0) || key0 + BC > seq_len) {
+      int thr = seq_len - 1 - key0 - 4 * hl;
+      if (CAUSAL) thr = min(thr, qrow - key0 - 4 * hl);
+#pragma unroll
+      for (int kb = 0; kb < TL::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kc = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const uint32_t dead = (uint32_t)((thr - kc) >> 31);
+          const uint32_t bits = __float_as_uint(s[kb][r]);
+          s[kb][r] = __uint_as_float((bits & ~dead) | (0xff800000u & dead));
+        }
+    }
+    // P = 2^(S·c - L2), dS = P ∘ (dP - D), packed as the B operand of dQ^T (key order of a
+    // contraction step c as in the forward's P~).
+    u32x4 dsw[TL::NPC];
+#pragma unroll
+    for (int c = 0; c < TL::NPC; ++c) {
+      const int kb = c >> 1, r0 = (c & 1) * 8;
+      float e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + u], p.c, -l2));
+        e[u] = pv * (dp[kb][r0 + u] - drow);
+      }
+      dsw[c] = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                       pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int c = 0; c < TL::NPC; ++c) {
+      const bf16x8 bf = as_bf16x8(dsw[c]);
+#pragma unroll
+      for (int db = 0; db < TL::NDB; ++db) {
+        const unsigned char* base = stage + 16 * c * TL::ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + taddr_lo[db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + taddr_hi[db]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf, dqacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  auto iteration = [&](int j, unsigned char* cur, unsigned char* nxt) {
+    if (j + 1 < nt) dma_tile(j + 1, nxt);
+    compute_tile(j, cur);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  dma_tile(0, lds0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < nt; j += 2) {
+    iteration(j, lds0, lds1);
+    if (j + 1 < nt) iteration(j + 1, lds1, lds0);
+  }
+
+  if (valid) {
+    uint16_t* out = p.dq + (row0 + (size_t)qrow) * D;
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w = {pack_bf16x2(dqacc[db][4 * g + 0] * p.scale, dqacc[db][4 * g + 1] * p.scale),
+                   pack_bf16x2(dqacc[db][4 * g + 2] * p.scale, dqacc[db][4 * g + 3] * p.scale)};
+        *(u32x2*)(out + db * 32 + 8 * g + 4 * hl) = w;
+      }
+  }
+}
+
+// ---- dK/dV kernel ----------------------------------------------------------------------
+
+template <int D, int BQ>
+struct DkvTile {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BK = 32 * WAVES;             // keys per workgroup
+  static constexpr int ROWB = 2 * D;
+  static constexpr int TILEB = BQ * ROWB;           // one Q (or dO) tile
+  static constexpr int VECB = 256;                  // one L (or D) vector, BQ fp32
+  static constexpr int STAGEB = 2 * TILEB + 2 * VECB;
+  static constexpr int LDS_BYTES = 2 * STAGEB;
+  static constexpr int DMA_PER_WAVE = TILEB / 1024 / WAVES;
+  static constexpr int NQB = BQ / 32;               // 32-query blocks per tile
+  static constexpr int NKC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int NPC = BQ / 16;
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(BQ == 64, "one 256-byte direct load per statistics vector");
+  static_assert(DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
+};
+
+template <int D, int BQ, bool CAUSAL, bool VARLEN, int OCC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(OCC, OCC)))
+void fa2_bwd_dkdv_kernel(BwdParams p) {
+  using TL = DkvTile<D, BQ>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  int bk, jb;
+  decode_bwd<CAUSAL, false>(p.nb * p.Hkv, p.nblk, p.heads_per_xcd, bk, jb);
+  const int bi = bk / p.Hkv;
+  const int hk = bk - bi * p.Hkv;
+  int tok0, seq_len;
+  seq_range<VARLEN>(p, bi, tok0, seq_len);
+  const int k0 = jb * TL::BK;
+  if (k0 >= seq_len) return;
+  const size_t kvrow0 = kv_plane<VARLEN>(p, bi, hk) + (size_t)tok0;
+
+  // This wave's 32 keys as B fragments of S = Q K^T and dP = dO V^T (key kw0 + l32).
+  const int kw0 = k0 + wave * 32;
+  const int krow = kw0 + l32;
+  const bool kvalid = krow < seq_len;
+  bf16x8 kf[TL::NKC], vf[TL::NKC];
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc) {
+    u32x4 tk = {0u, 0u, 0u, 0u}, tv = tk;
+    if (kvalid) {
+      const size_t off = (kvrow0 + (size_t)krow) * D + kc * 16 + hl * 8;
+      tk = *(const u32x4*)(p.k + off);
+      tv = *(const u32x4*)(p.v + off);
+    }
+    kf[kc] = as_bf16x8(tk ^ p.qflip);
+    vf[kc] = as_bf16x8(tv);
+  }
+
+  // Query tiles: causal starts at the tile holding query k0; every query head of the group.
+  const int t0 = CAUSAL ? k0 / BQ : 0;
+  const int ntq = (seq_len + BQ - 1) / BQ - t0;
+  const int nsteps = ntq * p.g;
+
+  int drow_[TL::DMA_PER_WAVE];
+  uint32_t doff[TL::DMA_PER_WAVE];
+#pragma unroll
+  for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+    const int b = wave * TL::DMA_PER_WAVE + d;
+    const int o = b * 1024 + lane * 16;
+    const int r = o / TL::ROWB;
+    const int pch = (o % TL::ROWB) / 16;
+    drow_[d] = r;
+    doff[d] = r * TL::ROWB + ((pch ^ dswz<D>(r)) * 16);
+  }
+  auto step_coords = [&](int s, int& q0, size_t& qrow0) {
+    const int hq = s / ntq;
+    q0 = (t0 + (s - hq * ntq)) * BQ;
+    qrow0 = q_plane<VARLEN>(p, bi, hk * p.g + hq) + (size_t)tok0;
+  };
+  auto dma_step = [&](int s, unsigned char* stage) {
+    int q0;
+    size_t qrow0;
+    step_coords(s, q0, qrow0);
+    const unsigned char* qt = (const unsigned char*)(p.q + (qrow0 + q0) * D);
+    const unsigned char* dt = (const unsigned char*)(p.dout + (qrow0 + q0) * D);
+    const uint32_t qs_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
+    const uint32_t ds_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
+    const int last = seq_len - 1 - q0;    // rows past the end re-read the last valid row
+#pragma unroll
+    for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
+      const uint32_t back = (uint32_t)(drow_[d] - min(drow_[d], last)) * TL::ROWB;
+      dma16(qt, doff[d] - back, qs_a + d * 1024);
+      dma16(dt, doff[d] - back, ds_a + d * 1024);
+    }
+    // Statistics of the tile's rows: L (wave 0) and D (wave 1), one dword per lane.
+    if (wave < 2) {
+      const float* src = (wave == 0 ? p.lse : p.delta) + qrow0 + q0;
+      const uint32_t voff = (uint32_t)min(lane, last) * 4u;
+      dma4(src, voff, lds_addr(stage + 2 * TL::TILEB + wave * TL::VECB));
+    }
+  };
+
+  // Row reads (A operands of S and dP): row qb*32 + l32, logical chunk 2kc + hl.
+  int raddr[TL::NKC];
+#pragma unroll
+  for (int kc = 0; kc < TL::NKC; ++kc)
+    raddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ dswz<D>(l32)) * 16);
+  // Transposed reads (A operands dO^T and Q^T), as K^T in the dQ kernel.
+  const int tr0 = 4 * hl + ((lane & 15) >> 2);
+  int taddr_lo[TL::NDB], taddr_hi[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) {
+    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    taddr_lo[db] = tr0 * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0)) * 16) + (col & 7) * 2;
+    taddr_hi[db] = (tr0 + 8) * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0 + 8)) * 16) + (col & 7) * 2;
+  }
+
+  f32x16 dkacc[TL::NDB], dvacc[TL::NDB];
+#pragma unroll
+  for (int db = 0; db < TL::NDB; ++db) {
+    dkacc[db] = (f32x16){};
+    dvacc[db] = (f32x16){};
+  }
+
+  auto compute_step = [&](int s_idx, const unsigned char* stage) {
+    int q0;
+    size_t qrow0;
+    step_coords(s_idx, q0, qrow0);
+    if ((CAUSAL && q0 + BQ - 1 < kw0) || kw0 >= seq_len) return;
+    // S = Q K^T and dP = dO V^T: lane = key, entries r = queries 32qb + 8(r/4) + 4hl + r%4.
+    f32x16 s[TL::NQB], dp[TL::NQB];
+#pragma unroll
+    for (int qb = 0; qb < TL::NQB; ++qb) {
+      s[qb] = (f32x16){};
+      dp[qb] = (f32x16){};
+#pragma unroll
+      for (int kc = 0; kc < TL::NKC; ++kc) {
+        const bf16x8 qa = *(const bf16x8*)(stage + qb * 32 * TL::ROWB + raddr[kc]);
+        const bf16x8 da = *(const bf16x8*)(stage + TL::TILEB + qb * 32 * TL::ROWB + raddr[kc]);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kc], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kc], dp[qb], 0, 0, 0);
+      }
+    }
+    // Masks: query < key (causal), query >= length (ragged tile). With off the entry's query
+    // offset minus 4hl (a constant), dead when off < lo or off > hi.
+    if ((CAUSAL && q0 < kw0 + 31) || q0 + BQ > seq_len) {
+      const int lo = krow - q0 - 4 * hl;
+      const int hi = seq_len - 1 - q0 - 4 * hl;
+#pragma unroll
+      for (int qb = 0; qb < TL::NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = qb * 32 + 8 * (r >> 2) + (r & 3);
+          uint32_t dead = (uint32_t)((hi - off) >> 31);
+          if (CAUSAL) dead |= (uint32_t)((off - lo) >> 31);
+          const uint32_t bits = __float_as_uint(s[qb][r]);
+          s[qb][r] = __uint_as_float((bits & ~dead) | (0xff800000u & dead));
+        }
+    }
+    // P and dS, packed as B operands (query order of contraction step c as the forward's
+    // key order of P~).
+    const unsigned char* lvec = stage + 2 * TL::TILEB;
+    const unsigned char* dvec = lvec + TL::VECB;
+    u32x4 pw[TL::NPC], dsw[TL::NPC];
+#pragma unroll
+    for (int c = 0; c < TL::NPC; ++c) {
+      const int qb = c >> 1, r0 = (c & 1) * 8;
+      float pe[8], de[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        // queries 32qb + 8(r/4) + 4hl + 0..3 for r = r0 + 4half .. +3
+        const int qo = qb * 32 + 8 * ((r0 >> 2) + half) + 4 * hl;
+        const float4 lv = *(const float4*)(lvec + 4 * qo);
+        const float4 dv = *(const float4*)(dvec + 4 * qo);
+        const float lq[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float dq[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int u = 4 * half + t;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][r0 + u], p.c, -lq[t] * kLog2e));
+          pe[u] = pv;
+          de[u] = pv * (dp[qb][r0 + u] - dq[t]);
+        }
+      }
+      pw[c] = (u32x4){pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]),
+                      pack_bf16x2(pe[4], pe[5]), pack_bf16x2(pe[6], pe[7])};
+      dsw[c] = (u32x4){pack_bf16x2(de[0], de[1]), pack_bf16x2(de[2], de[3]),
+                       pack_bf16x2(de[4], de[5]), pack_bf16x2(de[6], de[7])};
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+    for (int c = 0; c < TL::NPC; ++c) {
+      const bf16x8 pf = as_bf16x8(pw[c]);
+      const bf16x8 sf = as_bf16x8(dsw[c]);
+#pragma unroll
+      for (int db = 0; db < TL::NDB; ++db) {
+        const unsigned char* qbase = stage + 16 * c * TL::ROWB;
+        const unsigned char* dbase = stage + TL::TILEB + 16 * c * TL::ROWB;
+        const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + taddr_lo[db]));
+        const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + taddr_hi[db]));
+        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + taddr_lo[db]));
+        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + taddr_hi[db]));
+        const bf16x8 da = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 qa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, pf, dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf, dkacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  auto iteration = [&](int st, unsigned char* cur, unsigned char* nxt) {
+    if (st + 1 < nsteps) dma_step(st + 1, nxt);
+    compute_step(st, cur);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  dma_step(0, lds0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int st = 0; st < nsteps; st += 2) {
+    iteration(st, lds0, lds1);
+    if (st + 1 < nsteps) iteration(st + 1, lds1, lds0);
+  }
+
+  if (kvalid) {
+    uint16_t* kout = p.dk + (kvrow0 + (size_t)krow) * D;
+    uint16_t* vout = p.dv + (kvrow0 + (size_t)krow) * D;
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 wk = {pack_bf16x2(dkacc[db][4 * g + 0] * p.scale, dkacc[db][4 * g + 1] * p.scale),
+                    pack_bf16x2(dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale)};
+        u32x2 wv = {pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]),
+                    pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
+        *(u32x2*)(kout + db * 32 + 8 * g + 4 * hl) = wk;
+        *(u32x2*)(vout + db * 32 + 8 * g + 4 * hl) = wv;
+      }
+  }
+}
+
+// ---- host side ------------------------------------------------------------------------
+
+typedef const void* KernelFn;
+
+struct BwdKernels {
+  int dq_bc;
+  int dq_threads;
+  int dkdv_threads;
+  KernelFn dq[2][2];     // [varlen][causal]
+  KernelFn dkdv[2][2];
+};
+
+template <int D, int BC_DQ, int OCC_DKDV>
+BwdKernels make_bwd() {
+  BwdKernels k;
+  k.dq_bc = BC_DQ;
+  k.dq_threads = DqTile<D, BC_DQ>::THREADS;
+  k.dkdv_threads = DkvTile<D, 64>::THREADS;
+  k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false>;
+  k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false>;
+  k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true>;
+  k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true>;
+  k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, false, false, OCC_DKDV>;
+  k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, true, false, OCC_DKDV>;
+  k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, false, true, OCC_DKDV>;
+  k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, true, true, OCC_DKDV>;
+  return k;
+}
+
+const BwdKernels* bwd_kernels(int d) {
+  static const BwdKernels k64 = make_bwd<64, 64, 2>();
+  static const BwdKernels k128 = make_bwd<128, 32, 1>();
+  return d == 64 ? &k64 : d == 128 ? &k128 : nullptr;
+}
+
+bool aligned_to(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+int bwd_launch(const BwdKernels& kk, bool varlen, bool causal, BwdParams p, int nblk_q, int nblk_k,
+               long long npairs_q, long long npairs_k, void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
+  const int v = varlen ? 1 : 0, c = causal ? 1 : 0;
+  p.nblk = nblk_q;
+  p.heads_per_xcd = (npairs_q % 8 == 0) ? (int)(npairs_q / 8) : 0;
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel(kk.dq[v][c], dim3((unsigned)(nblk_q * npairs_q)),
+                                 dim3((unsigned)kk.dq_threads), args, 0, (hipStream_t)stream);
+  if (e != hipSuccess) return FA2_ERR_LAUNCH;
+  BwdParams p2 = p;
+  p2.nblk = nblk_k;
+  p2.heads_per_xcd = (npairs_k % 8 == 0) ? (int)(npairs_k / 8) : 0;
+  void* args2[] = {&p2};
+  e = hipLaunchKernel(kk.dkdv[v][c], dim3((unsigned)(nblk_k * npairs_k)),
+                      dim3((unsigned)kk.dkdv_threads), args2, 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, const void* dq, const void* dk, const void* dv, const float* delta,
+              int d, float scale) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA2_ERR_NULL_PTR;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  const void* b16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* ptr : b16)
+    if (!aligned_to(ptr, 16)) return FA2_ERR_MISALIGNED;
+  if (!aligned_to(lse, 4) || !aligned_to(delta, 4)) return FA2_ERR_MISALIGNED;
+  if (!isfinite(scale)) return FA2_ERR_BAD_SCALE;
+  return FA2_OK;
+}
+
+void bwd_fill(BwdParams& p, const void* q, const void* k, const void* v, const void* o,
+              const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
+              float scale) {
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.lse = lse;
+  p.dout = (const uint16_t*)dout;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.delta = delta;
+  p.c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
+  p.scale = scale;
+  p.qflip = scale < 0.f ? 0x80008000u : 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int H_kv,
+            int N, int d, int causal, float scale, void* stream) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N < 0) return FA2_ERR_BAD_SHAPE;
+  if (N == 0) return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
+  if (st != FA2_OK) return st;
+  const long long nblk = ((long long)N + 127) / 128;
+  const long long pq = (long long)B * H, pk = (long long)B * H_kv;
+  if (nblk * pq > 0x7fffffffLL || pq * (long long)N > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  BwdParams p;
+  bwd_fill(p, q, k, v, o, lse, dout, dq, dk, dv, delta, scale);
+  p.cu_seqlens = nullptr;
+  p.nb = B;
+  p.H = H;
+  p.Hkv = H_kv;
+  p.g = H / H_kv;
+  p.N = N;
+  p.T = N;
+  return bwd_launch(*bwd_kernels(d), false, causal != 0, p, (int)nblk, (int)nblk, pq, pk, stream);
+}
+
+int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, float* delta,
+                   const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens, int H,
+                   int H_kv, int d, int causal, float scale, void* stream) {
+  if (H <= 0 || H_kv <= 0 || H % H_kv != 0 || num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
+    return FA2_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
+    return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (!cu_seqlens) return FA2_ERR_NULL_PTR;
+  if (!aligned_to(cu_seqlens, 4)) return FA2_ERR_MISALIGNED;
+  int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
+  if (st != FA2_OK) return st;
+  const long long nblk = ((long long)max_seqlen + 127) / 128;
+  const long long pq = (long long)num_seqs * H, pk = (long long)num_seqs * H_kv;
+  if (nblk * pq > 0x7fffffffLL || (long long)H * total_tokens > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  BwdParams p;
+  bwd_fill(p, q, k, v, o, lse, dout, dq, dk, dv, delta, scale);
+  p.cu_seqlens = cu_seqlens;
+  p.nb = num_seqs;
+  p.H = H;
+  p.Hkv = H_kv;
+  p.g = H / H_kv;
+  p.N = max_seqlen;
+  p.T = total_tokens;
+  return bwd_launch(*bwd_kernels(d), true, causal != 0, p, (int)nblk, (int)nblk, pq, pk, stream);
+}
+
+}  // extern "C"

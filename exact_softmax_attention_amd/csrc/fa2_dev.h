@@ -1,0 +1,62 @@
+// fa2_dev.h — device-side helpers shared by the gfx950 attention kernels (forward and
+// backward): vector types, bf16 packing, direct global->LDS loads, LDS addressing and the
+// cross-half reductions of a 64-lane wave. Included by each kernel source; everything here
+// has internal linkage.
+#ifndef FA2_DEV_H_
+#define FA2_DEV_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 t = {(__bf16)lo, (__bf16)hi};               // round-to-nearest-even
+  return __builtin_bit_cast(uint32_t, t);
+}
+
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes at base + voff land at
+// LDS address lds + 16*l. base and lds are wave-uniform. Completion is tracked by vmcnt,
+// which the caller waits on explicitly before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)LDS_PTR(const void, p);
+}
+
+// Maximum over both 32-lane halves (lane l and l^32 hold the two halves of a row's keys).
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One direct global->LDS load of 4 bytes per lane: lane l's dword at base + voff lands at
+// LDS address lds + 4*l (256 bytes per wave).
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+}  // namespace
+
+#endif  // FA2_DEV_H_

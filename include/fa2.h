@@ -1,5 +1,6 @@
 /*
- * fa2.h — C ABI of the gfx950 exact-softmax-attention forward library (libfa2.so).
+ * fa2.h — C ABI of the gfx950 exact-softmax-attention library (libfa2.so): forward and
+ * backward.
  *
  * The operation (per head, per sequence):
  *     S = scale * Q K^T,  S[i][j] = -inf where causal and j > i,
@@ -117,6 +118,35 @@ int fa2_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, flo
                        const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
                        int H, int H_kv, int d, int causal, float scale, int variant,
                        void* stream);
+
+/*
+ * Backward: gradients of O = softmax(scale * Q K^T [causal]) V with respect to Q, K and V,
+ * given dO, the forward's O and LSE. P is recomputed from LSE rather than stored, and
+ *     D = rowsum(dO o O),  dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+ *     dQ = scale * dS K,   dK = scale * dS^T Q
+ * ("FlashAttention 2: ..." reading notes, papers.chlience.com, sections 5.2 and 5.3;
+ * paper-graph-ui summary, section 3.4, "The Backward Pass: Simpler Statistics, Same
+ * Structure"; the pages state dQ and dK for an unscaled score, the factor scale follows from
+ * S = scale * Q K^T). With grouped-query attention dK and dV of a key/value head are summed
+ * over its query heads (chlience notes, section 5.6).
+ *   q, o, dout, dq : bf16 [B, H, N, d];  k, v, dk, dv : bf16 [B, H_kv, N, d];
+ *   lse            : fp32 [B, H, N], the forward's logsumexp (natural log);
+ *   delta          : fp32 [B, H, N] caller-provided buffer, overwritten with D (it is the
+ *                    only intermediate; the library allocates nothing).
+ *   H_kv must divide H. d, causal and scale as for the forward (same scale as the forward).
+ *   dq, dk, dv and delta are fully overwritten on success; they must not alias the inputs.
+ * Two kernels run in order on stream (dQ and D, then dK and dV); no atomics are used, so the
+ * gradients are bitwise reproducible. Validation, ownership and zero-size rules as fa2_fwd.
+ * Varlen: q, o, dout, dq [H, T, d]; k, v, dk, dv [H_kv, T, d]; lse, delta [H, T];
+ * cu_seqlens as for fa2_fwd_varlen (tokens covered by no sequence are left unwritten).
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* delta,
+            int B, int H, int H_kv, int N, int d, int causal, float scale, void* stream);
+int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, float* delta,
+                   const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                   int H, int H_kv, int d, int causal, float scale, void* stream);
 
 /* Number of kernel variants for head dimension d (0 if d is unsupported). Host only. */
 int fa2_num_variants(int d);

@@ -41,6 +41,10 @@ Readings where the pages are silent:
   * a row with no allowed key (cannot happen for square causal or
     non-causal attention) would give O = 0 and LSE = -inf.
 
+The backward (gradients with respect to Q, K, V) is the same materialised
+definition differentiated by hand: chlience notes §5.3, paper-graph-ui §3.4
+"The Backward Pass: Simpler Statistics, Same Structure".
+
 Every function here is pinned by tests/test_oracle_pins.py (brute force,
 closed forms, library routines, invariants and the pages' online
 recurrence); none is "parity unpinned".
@@ -49,8 +53,9 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attention", "attention_gqa", "attention_head", "attention_rows", "attention_varlen",
-           "attention_varlen_gqa", "kv_head"]
+__all__ = ["attention", "attention_backward_gqa", "attention_backward_head", "attention_backward_varlen",
+           "attention_gqa", "attention_head", "attention_rows", "attention_varlen", "attention_varlen_gqa",
+           "kv_head"]
 
 
 def _as_f64(x) -> np.ndarray:
@@ -182,3 +187,74 @@ def attention_varlen_gqa(q, k, v, cu_seqlens, causal: bool, scale: float):
             hk = kv_head(h, H, H_kv)
             o[h, a:b], lse[h, a:b] = attention_head(q[h, a:b], k[hk, a:b], v[hk, a:b], causal, scale)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward (gradients of O with respect to Q, K, V for an upstream gradient dO)
+# ---------------------------------------------------------------------------
+
+def attention_backward_head(q, k, v, do, causal: bool, scale: float):
+    """Gradients of O = softmax(scale * Q K^T [causal]) V for one head, from the definition.
+
+    With P the materialised softmax (``_softmax_rows``) and O = P V:
+        dV = P^T dO,   dP = dO V^T,   D = rowsum(dO o O),   dS = P o (dP - D),
+        dQ = scale * dS K,   dK = scale * dS^T Q
+    (chlience notes §5.3; paper-graph-ui §3.4 "The Backward Pass: Simpler Statistics, Same
+    Structure", which also derives D = rowsum(P o dP) = rowsum(dO o O) from the softmax
+    Jacobian). The pages write dQ = dS K, dK = dS^T Q for an unscaled score; the factor
+    ``scale`` is the chain rule through S = scale * Q K^T. Masked entries have P = 0 and so
+    dS = 0. q, k, v, do: [N, d]; returns (dQ, dK, dV) in float64.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    n = q.shape[0]
+    if n == 0:
+        return np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    s = float(scale) * (q @ k.T)
+    if causal:
+        s[np.triu_indices(n, k=1)] = -np.inf
+    p, _ = _softmax_rows(s)
+    o = p @ v
+    dv = p.T @ do
+    dp = do @ v.T
+    dvec = np.sum(do * o, axis=1, keepdims=True)
+    ds = p * (dp - dvec)
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward_gqa(q, k, v, do, causal: bool, scale: float):
+    """Backward over q, do [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv | H): the gradient of a
+    key/value head is the sum over the query heads mapped to it (chlience notes §5.6).
+    Returns (dQ [B,H,N,d], dK [B,H_kv,N,d], dV [B,H_kv,N,d])."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    B, H = q.shape[:2]
+    H_kv = k.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            gq, gk, gv = attention_backward_head(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale)
+            dq[b, h] = gq
+            dk[b, hk] += gk
+            dv[b, hk] += gv
+    return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, do, cu_seqlens, causal: bool, scale: float):
+    """Packed backward: q, do [H, T, d]; k, v [H_kv, T, d]; sequences as in
+    ``attention_varlen``. Returns (dQ, dK, dV)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    H = q.shape[0]
+    H_kv = k.shape[0]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            gq, gk, gv = attention_backward_head(q[h, a:b], k[hk, a:b], v[hk, a:b], do[h, a:b], causal, scale)
+            dq[h, a:b] = gq
+            dk[hk, a:b] += gk
+            dv[hk, a:b] += gv
+    return dq, dk, dv

@@ -168,6 +168,45 @@ def test_gqa_empty_is_ok():
     assert _varlen_gqa(T=0, q=None, k=None, v=None, o=None, lse=None) == 0
 
 
+def _bwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE, B=1, H=4,
+         H_kv=2, N=64, d=128, causal=1, scale=0.088):
+    return fa2.load_library().fa2_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, H_kv, N, d, causal, scale,
+                                       None)
+
+
+def _bwd_varlen(cu=FAKE, S=2, maxlen=16, T=32, H=4, H_kv=4, d=64, causal=0, scale=0.125, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE)
+    p.update(ptrs)
+    return fa2.load_library().fa2_bwd_varlen(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"],
+                                              p["dv"], p["delta"], cu, S, maxlen, T, H, H_kv, d, causal, scale,
+                                              None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1), (dict(delta=None), 1),
+    (dict(B=0), 2), (dict(H_kv=3), 2), (dict(H_kv=0), 2), (dict(N=-1), 2),
+    (dict(d=96), 3), (dict(dq=FAKE + 8), 4), (dict(delta=FAKE + 2), 4), (dict(o=FAKE + 4), 4),
+    (dict(scale=float("nan")), 5), (dict(N=1 << 30, H=64, H_kv=64), 9),
+])
+def test_bwd_validation(kwargs, code):
+    assert _bwd(**kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(cu=None), 1), (dict(dv=None), 1), (dict(H_kv=3), 2), (dict(S=-1), 2), (dict(d=32), 3),
+    (dict(cu=FAKE + 2), 4), (dict(scale=float("inf")), 5),
+])
+def test_bwd_varlen_validation(kwargs, code):
+    assert _bwd_varlen(**kwargs) == code
+
+
+def test_bwd_empty_is_ok():
+    none = dict(q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None, delta=None)
+    assert _bwd(N=0, **none) == 0
+    assert _bwd_varlen(T=0, cu=None, **none) == 0
+
+
 def _gpu_present():
     if os.path.exists("/dev/kfd"):
         return True
@@ -185,6 +224,8 @@ def test_no_device_reported():
     assert _varlen() == 6
     assert _gqa() == 6
     assert _varlen_gqa() == 6
+    assert _bwd() == 6
+    assert _bwd_varlen() == 6
 
 
 def test_binding_rejects_cpu_tensors():
