@@ -139,6 +139,40 @@ def run(args):
         def step():
             fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, variant=args.variant)
 
+    merge_info = None
+    if args.split_kv:
+        if w.varlen or args.bwd or args.kv_heads:
+            raise SystemExit("--split-kv runs the forward of a fixed-length MHA workload")
+        S, N = args.split_kv, w.N
+        nq = args.q_rows or N
+        if N % S or not (0 < nq <= N):
+            raise SystemExit(f"--split-kv {S} must divide N={N}; 0 < --q-rows <= N")
+        step_k = N // S
+        qq = qd[:, :, N - nq:].contiguous()
+        o_parts = torch.empty((S,) + tuple(qq.shape), dtype=torch.bfloat16, device=dev)
+        l_parts = torch.empty((S,) + tuple(qq.shape[:3]), dtype=torch.float32, device=dev)
+        o = torch.empty_like(qq)
+        lse = torch.empty(qq.shape[:3], dtype=torch.float32, device=dev)
+        if nq < N:    # exact count of allowed (query, key) pairs, bottom-right causal
+            pairs = nq * (N - nq) + nq * (nq + 1) // 2 if w.causal else nq * N
+            flops = 4.0 * w.d * w.B * w.H * pairs
+
+        def step():   # all pieces in one launch, then the merge
+            fa2.fwd_splitkv(qq, kd, vd, S, causal=w.causal, diag=N - nq, scale=w.scale, out=o, lse=lse,
+                            o_parts=o_parts, lse_parts=l_parts, variant=args.variant)
+
+        def one_pass():
+            fa2.fwd_chunk(qq, kd, vd, causal=w.causal, diag=N - nq, scale=w.scale, out=o, lse=lse,
+                          variant=args.variant)
+
+        def merge_only():
+            fa2.lse_merge(o_parts, l_parts, out=o, lse=lse)
+
+        rows = qq.numel() // w.d
+        merge_info = {"parts": S, "q_rows": nq, "rows": rows,
+                      "merge_bytes": S * rows * (2 * w.d + 4) + rows * (2 * w.d + 4),
+                      "fns": (one_pass, merge_only)}
+
     if args.bwd:
         if w.varlen:
             raise SystemExit("--bwd runs on fixed-length workloads")
@@ -177,8 +211,33 @@ def run(args):
     ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
 
+    def time_fn(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    split_report = None
+    if merge_info is not None:
+        one_pass, merge_only = merge_info.pop("fns")
+        one_ms = time_fn(one_pass, args.steps)
+        merge_ms = time_fn(merge_only, max(args.steps, 20))
+        gbs = merge_info["merge_bytes"] / (merge_ms * 1e-3) / 1e9
+        split_report = dict(merge_info, one_pass_ms=round(one_ms, 5),
+                            one_pass_tflops=round(flops / (one_ms * 1e-3) / 1e12, 2),
+                            merge_ms=round(merge_ms, 5),
+                            merge_roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+
     traffic = None
-    t = load_traffic() if (w.name == "c4" and not args.kv_heads and args.variant == 0 and not args.bwd) else None
+    t = (load_traffic() if (w.name == "c4" and args.variant == 0 and not (args.kv_heads or args.bwd or args.split_kv))
+         else None)
     if t is not None:
         traffic = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
@@ -192,6 +251,10 @@ def run(args):
                                    f"{args.kv_heads} key/value heads", "H_kv": args.kv_heads})
     if args.bwd:
         config.update({"workload": f"backward of {config['workload']}", "kernel_variant": "bwd_dq+bwd_dkdv"})
+    if split_report is not None:
+        config.update({"workload": f"split-KV forward ({split_report['parts']} key pieces in one launch + LSE merge), last "
+                                   f"{split_report['q_rows']} queries of {config['workload']}",
+                       "split_kv": split_report})
     out = {
         "metric": ("attention bwd TFLOP/s (2.5 x 4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak" if args.bwd
                    else "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak"),
@@ -204,7 +267,7 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3)
-                        if w.name == "c4" and not (args.kv_heads or args.bwd) else None),
+                        if w.name == "c4" and not (args.kv_heads or args.bwd or args.split_kv) else None),
         "dtype": "bf16",
         "data": "synthetic",
         "config": config,
@@ -224,7 +287,7 @@ def run(args):
     }
     if args.cpu_baseline_heads > 0:
         out["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_baseline_heads)
-                               if not (w.varlen or args.kv_heads or args.bwd) else None)
+                               if not (w.varlen or args.kv_heads or args.bwd or args.split_kv) else None)
     print(json.dumps(out), flush=True)
 
 
@@ -269,6 +332,10 @@ def main():
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (dQ, dK, dV from dO, O, LSE) instead of the forward")
+    ap.add_argument("--split-kv", type=int, default=0,
+                    help="split the keys into this many pieces in one launch and merge them (fa2_fwd_splitkv)")
+    ap.add_argument("--q-rows", type=int, default=0,
+                    help="with --split-kv: only the last Q_ROWS queries (decode / chunked prefill shape)")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped-query attention: K/V with this many heads (must divide H; 0: H)")
     ap.add_argument("--cpu-baseline-heads", type=int, default=8,

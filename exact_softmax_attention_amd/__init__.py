@@ -14,12 +14,15 @@ from ._lib import (
     bwd,
     bwd_varlen,
     fwd,
+    fwd_chunk,
     fwd_gqa,
+    fwd_splitkv,
     fwd_varlen,
     fwd_varlen_gqa,
     geometry,
     lib_path,
     load_library,
+    lse_merge,
     num_variants,
     variant_name,
 )
@@ -31,12 +34,15 @@ __all__ = [
     "bwd",
     "bwd_varlen",
     "fwd",
+    "fwd_chunk",
     "fwd_gqa",
+    "fwd_splitkv",
     "fwd_varlen",
     "fwd_varlen_gqa",
     "geometry",
     "lib_path",
     "load_library",
+    "lse_merge",
     "num_variants",
     "variant_name",
 ]

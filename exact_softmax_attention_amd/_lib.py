@@ -32,6 +32,11 @@ _SIGNATURES = {
     "fa2_fwd_varlen_variant": ([_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_int, _c_void_p], _c_int),
     "fa2_fwd_gqa": ([_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_void_p], _c_int),
     "fa2_fwd_varlen_gqa": ([_c_void_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p], _c_int),
+    "fa2_fwd_chunk": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p], _c_int),
+    "fa2_fwd_splitkv": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p, _c_void_p, _c_int,
+                                                            _c_void_p], _c_int),
+    "fa2_lse_merge": ([_c_void_p, _c_void_p, _c_int, ctypes.c_longlong, _c_int, _c_void_p, _c_void_p, _c_void_p],
+                      _c_int),
     "fa2_bwd": ([_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
     "fa2_bwd_varlen": ([_c_void_p] * 11 + [_c_int] * 7 + [_c_float, _c_void_p], _c_int),
     "fa2_num_variants": ([_c_int], _c_int),
@@ -333,3 +338,102 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool 
                                 int(bool(causal)), float(scale), _stream_ptr(q.device))
     _check(st)
     return dq, dk, dv
+
+
+def fwd_chunk(q, k, v, causal: bool = False, diag: int = 0, scale: float | None = None, out=None, lse=None,
+              variant: int = 0):
+    """Forward of q bf16 [B, H, N_q, d] against one key/value chunk k, v bf16 [B, H_kv, N_k, d].
+
+    Causal: query i may attend key j iff j <= i + diag. Rows with no allowed key get O = 0,
+    LSE = -inf. Returns (o bf16 [B, H, N_q, d], lse fp32 [B, H, N_q]).
+    """
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    if k.shape != v.shape:
+        raise ValueError("k, v shapes differ")
+    B, H, N_q, d = q.shape
+    H_kv, N_k = k.shape[1], k.shape[2]
+    if (k.shape[0], k.shape[3]) != (B, d):
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", out, torch.bfloat16, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    if out.shape != q.shape or tuple(lse.shape) != (B, H, N_q):
+        raise ValueError("out/lse shape mismatch")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_fwd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, H_kv, N_q, N_k, d, int(bool(causal)), int(diag), float(scale), int(variant),
+                               _stream_ptr(q.device))
+    _check(st)
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse=None):
+    """Merge partial results: o_parts bf16 [S, ..., d], lse_parts fp32 [S, ...] (same leading
+    shape) -> (o bf16 [..., d], lse fp32 [...]) with LSE = log sum exp(LSE_s) and
+    O = sum exp(LSE_s - LSE) O_s."""
+    torch = _torch()
+    _check_tensor("o_parts", o_parts, torch.bfloat16, o_parts.dim())
+    _check_tensor("lse_parts", lse_parts, torch.float32, lse_parts.dim())
+    if o_parts.dim() < 2 or tuple(o_parts.shape[:-1]) != tuple(lse_parts.shape):
+        raise ValueError("o_parts must be [S, ..., d] with lse_parts [S, ...]")
+    S, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts.numel() // S if S else 0
+    out = torch.empty(o_parts.shape[1:], dtype=torch.bfloat16, device=o_parts.device) if out is None else out
+    lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device) if lse is None else lse
+    _check_tensor("out", out, torch.bfloat16, out.dim())
+    _check_tensor("lse", lse, torch.float32, lse.dim())
+    if tuple(out.shape) != tuple(o_parts.shape[1:]) or tuple(lse.shape) != tuple(lse_parts.shape[1:]):
+        raise ValueError("out/lse shape mismatch")
+    lib = load_library()
+    with torch.cuda.device(o_parts.device):
+        st = lib.fa2_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, rows, d, out.data_ptr(), lse.data_ptr(),
+                               _stream_ptr(o_parts.device))
+    _check(st)
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, num_splits: int, causal: bool = False, diag: int = 0, scale: float | None = None,
+                out=None, lse=None, o_parts=None, lse_parts=None, variant: int = 0):
+    """``fwd_chunk`` with the keys split into up to ``num_splits`` pieces computed in one launch
+    and merged by LSE. ``o_parts`` (bf16 [S, B, H, N_q, d]) and ``lse_parts`` (fp32
+    [S, B, H, N_q]) are the workspace; allocated when not given."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    if k.shape != v.shape:
+        raise ValueError("k, v shapes differ")
+    B, H, N_q, d = q.shape
+    H_kv, N_k = k.shape[1], k.shape[2]
+    if (k.shape[0], k.shape[3]) != (B, d):
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    S = int(num_splits)
+    if S < 1:
+        raise ValueError("num_splits must be >= 1")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o_parts is None:
+        o_parts = torch.empty((S, B, H, N_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse_parts is None:
+        lse_parts = torch.empty((S, B, H, N_q), dtype=torch.float32, device=q.device)
+    _check_tensor("out", out, torch.bfloat16, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    _check_tensor("o_parts", o_parts, torch.bfloat16, 5)
+    _check_tensor("lse_parts", lse_parts, torch.float32, 4)
+    if out.shape != q.shape or tuple(lse.shape) != (B, H, N_q) or tuple(o_parts.shape) != (S, B, H, N_q, d) \
+            or tuple(lse_parts.shape) != (S, B, H, N_q):
+        raise ValueError("out/lse/o_parts/lse_parts shape mismatch")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 B, H, H_kv, N_q, N_k, d, int(bool(causal)), int(diag), float(scale), S,
+                                 o_parts.data_ptr(), lse_parts.data_ptr(), int(variant), _stream_ptr(q.device))
+    _check(st)
+    return out, lse

@@ -13,7 +13,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SRCS = [os.path.join(PKG_DIR, "csrc", "fa2_fwd.hip"), os.path.join(PKG_DIR, "csrc", "fa2_bwd.hip")]
+SRCS = [os.path.join(PKG_DIR, "csrc", name) for name in ("fa2_fwd.hip", "fa2_bwd.hip", "fa2_merge.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG_DIR, "libfa2.so")
 ARCH = "gfx950"

@@ -69,7 +69,11 @@ struct Params {
   int H;                  // query heads
   int Hkv;                // key/value heads (H for MHA)
   int g;                  // query heads per key/value head, H / Hkv
-  int N;                  // sequence length, or max_seqlen (varlen)
+  int N;                  // query rows per sequence, or max_seqlen (varlen)
+  int Nk;                 // keys per sequence (fixed length; varlen uses the sequence length)
+  int diag;               // causal: query i may attend key j iff j <= i + diag
+  int split_len;          // keys per split (split-KV: blockIdx.y selects the split); Nk if none
+  long long part_rows;    // split s writes O/LSE rows s * part_rows + ... (0 if not split)
   int T;                  // tokens per head plane: N, or total_tokens (varlen)
   int tr;                 // row blocks per (batch|sequence, head)
   int heads_per_xcd;      // > 0: XCD-aware workgroup order (nb*H divisible by 8)
@@ -164,7 +168,7 @@ void fa2_fwd_kernel(Params p) {
   decode_block<CAUSAL>(p, bh, i);
   const int bi = bh / p.H;
   const int h = bh - bi * p.H;
-  int seq_len;
+  int seq_len, seq_k;   // query rows and keys of this sequence
   // Grouped/multi-query attention: query head h reads key/value head h / g, so the g query
   // heads of a group share one K/V plane without copies.
   const int hk = h / p.g;
@@ -176,13 +180,24 @@ void fa2_fwd_kernel(Params p) {
     a = min(max(a, 0), p.T);
     e = min(max(e, a), p.T);
     seq_len = e - a;
+    seq_k = seq_len;
     row0 = (size_t)h * (size_t)p.T + (size_t)a;
     kvrow0 = (size_t)hk * (size_t)p.T + (size_t)a;
   } else {
     seq_len = p.N;
+    seq_k = p.Nk;
     row0 = (size_t)bh * (size_t)p.N;
-    kvrow0 = ((size_t)bi * (size_t)p.Hkv + (size_t)hk) * (size_t)p.N;
+    kvrow0 = ((size_t)bi * (size_t)p.Hkv + (size_t)hk) * (size_t)p.Nk;
   }
+  // Split-KV: split s of the launch owns keys [s*split_len, (s+1)*split_len) and writes its
+  // partial O and LSE to part s of the output (rows offset by s*part_rows).
+  const int ks0 = VARLEN ? 0 : (int)blockIdx.y * p.split_len;
+  if (!VARLEN) {
+    seq_k = max(min(p.split_len, seq_k - ks0), 0);
+    kvrow0 += (size_t)ks0;
+  }
+  const int diag = p.diag - ks0;
+  const size_t orow0 = row0 + (VARLEN ? 0 : (size_t)blockIdx.y * (size_t)p.part_rows);
   const int q0 = i * TL::BR;
   if (q0 >= seq_len) return;  // uniform over the workgroup (varlen rows past the end)
 
@@ -190,8 +205,9 @@ void fa2_fwd_kernel(Params p) {
   const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
   const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
 
-  // Key tiles to visit: causal stops after the tile holding this block's last query.
-  const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
+  // Key tiles to visit: causal stops after the tile holding the last key this block's last
+  // query may attend (none when the whole key range lies after it).
+  const int kv_end = max(CAUSAL ? min(seq_k, q0 + TL::BR + diag) : seq_k, 0);
   const int nt = (kv_end + BC - 1) / BC;
 
   // ---- a2: this wave's 32 query rows as MFMA B fragments (Q^T), once -----------------
@@ -230,7 +246,7 @@ void fa2_fwd_kernel(Params p) {
     const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
     const uint32_t ks_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
     const uint32_t vs_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
-    if (key0 + BC <= seq_len) {
+    if (key0 + BC <= seq_k) {
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
         dma16(kt, koff[d], ks_a + d * 1024);
@@ -239,7 +255,7 @@ void fa2_fwd_kernel(Params p) {
     } else {
       // Ragged last tile: rows past the end re-read the last valid row, so every value in
       // LDS is finite (its probability is zero after the mask).
-      const int last = seq_len - 1 - key0;
+      const int last = seq_k - 1 - key0;
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
         const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * TL::ROWB;
@@ -277,7 +293,7 @@ void fa2_fwd_kernel(Params p) {
     const int key0 = j * BC;
     // a5: a wave whose rows all precede this tile's first key, or whose rows are all past
     // the end of the sequence, has nothing to add here.
-    if ((CAUSAL && key0 > qw0 + 31) || qw0 >= seq_len) return;
+    if ((CAUSAL && key0 > qw0 + 31 + diag) || qw0 >= seq_len) return;
     const unsigned char* ks = stage;
 
     // ---- a4: S^T = K_j Q^T ----------------------------------------------------------
@@ -306,9 +322,9 @@ void fa2_fwd_kernel(Params p) {
     // Entry (kb, r) of this lane is key key0 + koffs with koffs = kb*32 + 8*(r/4) + 4*hl + r%4.
     // It is dead when koffs - 4*hl exceeds thr (causal: key > query; ragged: key >= length),
     // a per-lane threshold; the sign of thr - const selects -inf with one bitfield insert.
-    if ((CAUSAL && key0 + BC - 1 > qw0) || key0 + BC > seq_len) {
-      int thr = seq_len - 1 - key0 - 4 * hl;
-      if (CAUSAL) thr = min(thr, qrow - key0 - 4 * hl);
+    if ((CAUSAL && key0 + BC - 1 > qw0 + diag) || key0 + BC > seq_k) {
+      int thr = seq_k - 1 - key0 - 4 * hl;
+      if (CAUSAL) thr = min(thr, qrow + diag - key0 - 4 * hl);
 #pragma unroll
       for (int kb = 0; kb < TL::NKB; ++kb)
 #pragma unroll
@@ -420,7 +436,7 @@ void fa2_fwd_kernel(Params p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  dma_tile(0, lds0);
+  if (nt > 0) dma_tile(0, lds0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int j = 0; j < nt; j += 2) {
@@ -432,7 +448,7 @@ void fa2_fwd_kernel(Params p) {
   const float l_tot = halves_sum(l_run);
   if (qrow < seq_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = p.o + (row0 + (size_t)qrow) * D;
+    uint16_t* orow = p.o + (orow0 + (size_t)qrow) * D;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
@@ -442,7 +458,7 @@ void fa2_fwd_kernel(Params p) {
         *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
       }
     if (hl == 0) {
-      p.lse[row0 + (size_t)qrow] =
+      p.lse[orow0 + (size_t)qrow] =
           l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
   }
@@ -502,7 +518,7 @@ void fa2_fwd_kernel_pp(Params p) {
   decode_block<CAUSAL>(p, bh, i);
   const int bi = bh / p.H;
   const int h = bh - bi * p.H;
-  int seq_len;
+  int seq_len, seq_k;
   const int hk = h / p.g;
   size_t row0, kvrow0;
   if (VARLEN) {
@@ -511,26 +527,39 @@ void fa2_fwd_kernel_pp(Params p) {
     a = min(max(a, 0), p.T);
     e = min(max(e, a), p.T);
     seq_len = e - a;
+    seq_k = seq_len;
     row0 = (size_t)h * (size_t)p.T + (size_t)a;
     kvrow0 = (size_t)hk * (size_t)p.T + (size_t)a;
   } else {
     seq_len = p.N;
+    seq_k = p.Nk;
     row0 = (size_t)bh * (size_t)p.N;
-    kvrow0 = ((size_t)bi * (size_t)p.Hkv + (size_t)hk) * (size_t)p.N;
+    kvrow0 = ((size_t)bi * (size_t)p.Hkv + (size_t)hk) * (size_t)p.Nk;
   }
+  // Split-KV: split s of the launch owns keys [s*split_len, (s+1)*split_len) and writes its
+  // partial O and LSE to part s of the output (rows offset by s*part_rows).
+  const int ks0 = VARLEN ? 0 : (int)blockIdx.y * p.split_len;
+  if (!VARLEN) {
+    seq_k = max(min(p.split_len, seq_k - ks0), 0);
+    kvrow0 += (size_t)ks0;
+  }
+  const int diag = p.diag - ks0;
+  const size_t orow0 = row0 + (VARLEN ? 0 : (size_t)blockIdx.y * (size_t)p.part_rows);
   const int q0 = i * TL::BR;
   if (q0 >= seq_len) return;
 
   const uint16_t* __restrict__ qh = p.q + row0 * D;
   const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
   const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
-  const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
+  const int kv_end = max(CAUSAL ? min(seq_k, q0 + TL::BR + diag) : seq_k, 0);
   const int nt = (kv_end + BC - 1) / BC;
 
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
   // Tiles this wave computes: causal tile j matters iff its first key <= the wave's last row.
-  const int ntw = (qw0 >= seq_len) ? 0 : (CAUSAL ? min(nt, (qw0 + 31) / BC + 1) : nt);
+  const int last_key = qw0 + 31 + diag;
+  const int ntw = (qw0 >= seq_len) ? 0
+                  : (CAUSAL ? (last_key < 0 ? 0 : min(nt, last_key / BC + 1)) : nt);
 
   // ---- a2: Q^T fragments ----------------------------------------------------------------
   bf16x8 qf[TL::NKC];
@@ -564,14 +593,14 @@ void fa2_fwd_kernel_pp(Params p) {
     const uint32_t st = lds_base + (uint32_t)(j & (TL::NSTAGE - 1)) * TL::STAGEB;
     const uint32_t ks_a = st + wave * TL::DMA_PER_WAVE * 1024;
     const uint32_t vs_a = st + TL::TILEB + wave * TL::DMA_PER_WAVE * 1024;
-    if (key0 + BC <= seq_len) {
+    if (key0 + BC <= seq_k) {
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
         dma16(kt, koff[d], ks_a + d * 1024);
         dma16(vt, voff[d], vs_a + d * 1024);
       }
     } else {
-      const int last = seq_len - 1 - key0;   // rows past the end re-read the last valid row
+      const int last = seq_k - 1 - key0;   // rows past the end re-read the last valid row
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
         const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * TL::ROWB;
@@ -661,9 +690,9 @@ void fa2_fwd_kernel_pp(Params p) {
   auto valu_phase = [&](int j) {
     if (j >= ntw) return;
     const int key0 = j * BC;
-    if ((CAUSAL && key0 + BC - 1 > qw0) || key0 + BC > seq_len) {
-      int thr = seq_len - 1 - key0 - 4 * hl;
-      if (CAUSAL) thr = min(thr, qrow - key0 - 4 * hl);
+    if ((CAUSAL && key0 + BC - 1 > qw0 + diag) || key0 + BC > seq_k) {
+      int thr = seq_k - 1 - key0 - 4 * hl;
+      if (CAUSAL) thr = min(thr, qrow + diag - key0 - 4 * hl);
 #pragma unroll
       for (int kb = 0; kb < TL::NKB; ++kb)
 #pragma unroll
@@ -707,7 +736,7 @@ void fa2_fwd_kernel_pp(Params p) {
   };
 
   // ---- the phase loop ------------------------------------------------------------------
-  dma_tile(0);
+  if (nt > 0) dma_tile(0);
   if (nt > 1) dma_tile(1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -734,7 +763,7 @@ void fa2_fwd_kernel_pp(Params p) {
   const float l_tot = halves_sum(l_run);
   if (qrow < seq_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = p.o + (row0 + (size_t)qrow) * D;
+    uint16_t* orow = p.o + (orow0 + (size_t)qrow) * D;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
@@ -744,7 +773,7 @@ void fa2_fwd_kernel_pp(Params p) {
         *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
       }
     if (hl == 0) {
-      p.lse[row0 + (size_t)qrow] =
+      p.lse[orow0 + (size_t)qrow] =
           l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
   }
@@ -841,12 +870,13 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
   return FA2_OK;
 }
 
-int launch(const Variant& var, bool varlen, bool causal, Params& p, int num_wg, void* stream) {
+int launch(const Variant& var, bool varlen, bool causal, Params& p, int num_wg, void* stream,
+           int grid_y = 1) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
   KernelFn fn = varlen ? var.varlen[causal ? 1 : 0] : var.fixed[causal ? 1 : 0];
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)num_wg), dim3((unsigned)var.threads), args, 0,
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)num_wg, (unsigned)grid_y), dim3((unsigned)var.threads), args, 0,
                                  (hipStream_t)stream);
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
@@ -859,6 +889,62 @@ void fill_scale(Params& p, float scale) {
 }
 
 int heads_per_xcd(long long nbh) { return (nbh % 8 == 0) ? (int)(nbh / 8) : 0; }
+
+// Shared body of fa2_fwd_chunk (num_splits == 1) and fa2_fwd_splitkv. With splits, the keys are
+// cut into ns contiguous pieces of split_len keys (a multiple of the key tile), one launch
+// computes every (row block, piece) pair into the caller's o_parts / lse_parts, and the LSE
+// merge combines the pieces into o / lse.
+int fwd_chunk_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int H_kv, int N_q, int N_k, int d, int causal, int diag, float scale,
+                   int variant, int num_splits, void* o_parts, float* lse_parts, void* stream) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N_q < 0 || N_k < 0)
+    return FA2_ERR_BAD_SHAPE;
+  if (diag < -(1 << 30) || diag > (1 << 30)) return FA2_ERR_BAD_SHAPE;
+  if (N_q == 0) return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (N_k == 0) k = v = q;   // never read: every row gets O = 0, LSE = -inf
+  const Variant* var = nullptr;
+  int st = check_common(q, k, v, o, lse, d, scale, variant, &var);
+  if (st != FA2_OK) return st;
+  const long long tr = ((long long)N_q + var->br - 1) / var->br;
+  const long long nbh = (long long)B * H;
+  const long long wg = tr * nbh;
+  // Element offsets are 64-bit in the kernel; the grid and row indices must fit 31 bits.
+  if (wg > 0x7fffffffLL || nbh * (long long)N_q > 0x7fffffffLL ||
+      (long long)B * H_kv * (long long)N_k > 0x7fffffffLL)
+    return FA2_ERR_TOO_LARGE;
+  int split_len = N_k, ns = 1;
+  if (num_splits > 1 && N_k > 0) {
+    if (!o_parts || !lse_parts) return FA2_ERR_NULL_PTR;
+    if (!aligned(o_parts, 16) || !aligned(lse_parts, 4)) return FA2_ERR_MISALIGNED;
+    if (num_splits > 65535) return FA2_ERR_TOO_LARGE;
+    const int per = (N_k + num_splits - 1) / num_splits;
+    split_len = (per + var->bc - 1) / var->bc * var->bc;
+    ns = (N_k + split_len - 1) / split_len;
+  }
+  Params p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)(ns > 1 ? o_parts : o);
+  p.lse = ns > 1 ? lse_parts : lse;
+  p.cu_seqlens = nullptr;
+  p.nb = B;
+  p.H = H;
+  p.Hkv = H_kv;
+  p.g = H / H_kv;
+  p.N = N_q;
+  p.Nk = N_k;
+  p.diag = diag;
+  p.split_len = split_len;
+  p.part_rows = ns > 1 ? nbh * N_q : 0;
+  p.T = N_q;
+  p.tr = (int)tr;
+  p.heads_per_xcd = heads_per_xcd(nbh);
+  fill_scale(p, scale);
+  st = launch(*var, false, causal != 0, p, (int)wg, stream, ns);
+  if (st != FA2_OK || ns == 1) return st;
+  return fa2_lse_merge(o_parts, lse_parts, ns, nbh * N_q, d, o, lse, stream);
+}
 
 }  // namespace
 
@@ -914,35 +1000,24 @@ int fa2_fwd_geometry(int B, int H, int N, int d, int causal, int variant, int* n
   return FA2_OK;
 }
 
+int fa2_fwd_chunk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int H_kv, int N_q, int N_k, int d, int causal, int diag, float scale, int variant,
+                  void* stream) {
+  return fwd_chunk_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, causal, diag, scale, variant, 1,
+                        nullptr, nullptr, stream);
+}
+
+int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int H_kv, int N_q, int N_k, int d, int causal, int diag, float scale,
+                    int num_splits, void* o_parts, float* lse_parts, int variant, void* stream) {
+  if (num_splits < 1) return FA2_ERR_BAD_SHAPE;
+  return fwd_chunk_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, causal, diag, scale, variant,
+                        num_splits, o_parts, lse_parts, stream);
+}
+
 int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int H_kv, int N, int d, int causal, float scale, int variant, void* stream) {
-  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N < 0) return FA2_ERR_BAD_SHAPE;
-  if (N == 0) return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
-  const Variant* var = nullptr;
-  int st = check_common(q, k, v, o, lse, d, scale, variant, &var);
-  if (st != FA2_OK) return st;
-  const long long tr = ((long long)N + var->br - 1) / var->br;
-  const long long nbh = (long long)B * H;
-  const long long wg = tr * nbh;
-  // Element offsets are 64-bit in the kernel; the grid and row indices must fit 31 bits.
-  if (wg > 0x7fffffffLL || nbh * (long long)N > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
-  Params p;
-  p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)k;
-  p.v = (const uint16_t*)v;
-  p.o = (uint16_t*)o;
-  p.lse = lse;
-  p.cu_seqlens = nullptr;
-  p.nb = B;
-  p.H = H;
-  p.Hkv = H_kv;
-  p.g = H / H_kv;
-  p.N = N;
-  p.T = N;
-  p.tr = (int)tr;
-  p.heads_per_xcd = heads_per_xcd(nbh);
-  fill_scale(p, scale);
-  return launch(*var, false, causal != 0, p, (int)wg, stream);
+  return fa2_fwd_chunk(q, k, v, o, lse, B, H, H_kv, N, N, d, causal, 0, scale, variant, stream);
 }
 
 int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -985,6 +1060,10 @@ int fa2_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, flo
   p.Hkv = H_kv;
   p.g = H / H_kv;
   p.N = max_seqlen;
+  p.Nk = max_seqlen;
+  p.diag = 0;
+  p.split_len = max_seqlen;
+  p.part_rows = 0;
   p.T = total_tokens;
   p.tr = (int)tr;
   p.heads_per_xcd = heads_per_xcd(nbh);

@@ -1,0 +1,92 @@
+// fa2_merge.hip — merge of partial attention results by their logsumexp (gfx950), and its C
+// ABI (declared in include/fa2.h).
+//
+// Attention over a key set that is split into parts (key/value chunks on one GPU, or shards
+// of the key sequence on several) is recovered exactly from each part's normalised output
+// O_s and logsumexp LSE_s:
+//     LSE = log sum_s exp(LSE_s),    O = sum_s exp(LSE_s - LSE) O_s
+// This is the same rescaling the online softmax applies between key blocks, applied once
+// across parts ("FlashAttention" on llm-infra-atlas: section 5 describes context parallelism
+// as one FlashAttention call per key shard with the right mask; the reading table of its
+// section 0 lists sparse variants that combine two variable-length calls by mixing their
+// LSEs). A part in which a row has no allowed key carries O_s = 0 and LSE_s = -inf and gets
+// weight zero; a row with no allowed key in any part gets O = 0 and LSE = -inf.
+//
+// The kernel is bound by HBM bandwidth (it reads every part once and writes the result once):
+// a row of D bf16 is handled by D/8 lanes, 16 bytes each, so every part's row is one
+// contiguous, fully used read. Weights are computed in fp32 with the base-2 exponential.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa2.h"
+#include "fa2_dev.h"
+
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void fa2_lse_merge_kernel(const uint16_t* __restrict__ o_parts,
+                                                            const float* __restrict__ lse_parts,
+                                                            int num_parts, long long rows,
+                                                            uint16_t* __restrict__ o,
+                                                            float* __restrict__ lse) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPB = 256 / LPR;      // rows per workgroup
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  if (row >= rows) return;
+
+  float m = -INFINITY;
+  for (int s = 0; s < num_parts; ++s) m = fmaxf(m, lse_parts[(size_t)s * rows + row]);
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float z = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < num_parts; ++s) {
+      const float w = __builtin_amdgcn_exp2f((lse_parts[(size_t)s * rows + row] - m) * kLog2e);
+      const u32x4 t = *(const u32x4*)(o_parts + ((size_t)s * rows + row) * D + part * 8);
+      z += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += w * __uint_as_float(t[e] << 16);
+        acc[2 * e + 1] += w * __uint_as_float(t[e] & 0xffff0000u);
+      }
+    }
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  const u32x4 out = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *(u32x4*)(o + (size_t)row * D + part * 8) = out;
+  if (part == 0) lse[row] = z > 0.f ? m + __builtin_amdgcn_logf(z) * kLn2 : -INFINITY;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, long long rows,
+                  int d, void* o, float* lse, void* stream) {
+  if (num_parts <= 0 || rows < 0) return FA2_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (rows == 0) return FA2_OK;
+  if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL_PTR;
+  if (!aligned16(o_parts) || !aligned16(o) || ((uintptr_t)lse_parts & 3) || ((uintptr_t)lse & 3))
+    return FA2_ERR_MISALIGNED;
+  const int rpb = 256 / (d / 8);
+  const long long blocks = (rows + rpb - 1) / rpb;
+  if (blocks > 0x7fffffffLL || (long long)num_parts * rows > (1LL << 40)) return FA2_ERR_TOO_LARGE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
+  const void* fn = d == 64 ? (const void*)&fa2_lse_merge_kernel<64> : (const void*)&fa2_lse_merge_kernel<128>;
+  const uint16_t* op = (const uint16_t*)o_parts;
+  uint16_t* oo = (uint16_t*)o;
+  void* args[] = {&op, &lse_parts, &num_parts, &rows, &oo, &lse};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // extern "C"

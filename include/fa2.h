@@ -120,6 +120,60 @@ int fa2_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, flo
                        void* stream);
 
 /*
+ * Forward of a query block against one key/value chunk, with separate query and key
+ * lengths: the building block of split-KV (several chunks, then fa2_lse_merge) and of
+ * sharding the key sequence across devices ("FlashAttention", llm-infra-atlas, section 5:
+ * each step of context parallelism is one call with the right mask).
+ *   q, o : bf16 [B, H, N_q, d];  k, v : bf16 [B, H_kv, N_k, d];  lse : fp32 [B, H, N_q].
+ *   causal: query i (0-based within q) may attend key j (0-based within k) iff
+ *           j <= i + diag. diag = 0 with N_q == N_k is fa2_fwd's mask; diag = N_k - N_q
+ *           aligns the last query with the last key; for the chunk [a, b) of a sequence
+ *           whose queries start at position q_start, diag = q_start - a. |diag| <= 2^30.
+ *   Rows with no allowed key (N_k == 0, or all keys masked) get O = 0 and LSE = -inf.
+ *   k and v are not read when N_k == 0 and may then be NULL.
+ * H_kv, variant and everything else as for fa2_fwd_gqa; fa2_fwd_gqa is this call with
+ * N_q = N_k = N and diag = 0.
+ */
+int fa2_fwd_chunk(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int H_kv, int N_q, int N_k, int d, int causal, int diag,
+                  float scale, int variant, void* stream);
+
+/*
+ * Split-KV forward: fa2_fwd_chunk's result computed with the keys cut into up to num_splits
+ * contiguous pieces that run in the same launch (more workgroups when B*H*ceil(N_q/128) is
+ * small, e.g. few query rows over a long key sequence), followed by fa2_lse_merge of the
+ * pieces. Arguments as fa2_fwd_chunk, plus:
+ *   num_splits : >= 1. The pieces are ceil(N_k / num_splits) keys rounded up to the key tile
+ *                of the variant, so fewer pieces than num_splits may be used.
+ *   o_parts    : bf16 [num_splits, B, H, N_q, d] workspace, lse_parts : fp32
+ *                [num_splits, B, H, N_q] workspace (caller-provided; overwritten; unused and
+ *                may be NULL when num_splits == 1 or N_k == 0).
+ * Results equal fa2_fwd_chunk's up to rounding (each piece's O is rounded to bf16 once
+ * before the merge).
+ */
+int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int H_kv, int N_q, int N_k, int d, int causal, int diag,
+                    float scale, int num_splits, void* o_parts, float* lse_parts, int variant,
+                    void* stream);
+
+/*
+ * Merge of partial results by their logsumexp (the "LSE mix"):
+ *     LSE = log sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s
+ * which recovers attention over the union of the parts' key sets exactly (up to rounding).
+ * ("FlashAttention", llm-infra-atlas: section 5 on context parallelism, and its section 0
+ * reading table on mixing the LSEs of two variable-length calls.)
+ *   o_parts   : bf16 [num_parts, rows, d] (part s is the contiguous block s), read only.
+ *   lse_parts : fp32 [num_parts, rows] (natural log; -inf marks a row with no key in part s).
+ *   o         : bf16 [rows, d]; lse : fp32 [rows]; written. rows is any count, e.g.
+ *               B * H * N_q for fa2_fwd_chunk outputs. o/lse must not alias the parts.
+ *   d         : 64 or 128.  num_parts >= 1.
+ * A row whose LSE_s are all -inf gets O = 0 and LSE = -inf. rows == 0 succeeds without a
+ * launch. Validation, ownership and asynchrony as for fa2_fwd.
+ */
+int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, long long rows,
+                  int d, void* o, float* lse, void* stream);
+
+/*
  * Backward: gradients of O = softmax(scale * Q K^T [causal]) V with respect to Q, K and V,
  * given dO, the forward's O and LSE. P is recomputed from LSE rather than stored, and
  *     D = rowsum(dO o O),  dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),

@@ -53,7 +53,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attention", "attention_backward_gqa", "attention_backward_head", "attention_backward_varlen",
+__all__ = ["attention", "attention_chunk", "attention_chunk_head", "lse_merge", "attention_backward_gqa", "attention_backward_head", "attention_backward_varlen",
            "attention_gqa", "attention_head", "attention_rows", "attention_varlen", "attention_varlen_gqa",
            "kv_head"]
 
@@ -258,3 +258,59 @@ def attention_backward_varlen(q, k, v, do, cu_seqlens, causal: bool, scale: floa
             dk[hk, a:b] += gk
             dv[hk, a:b] += gv
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Key/value chunks and the merge of partial results by their logsumexp
+# ---------------------------------------------------------------------------
+
+def attention_chunk_head(q, k, v, causal: bool, diag: int, scale: float):
+    """Attention of q [N_q, d] over one key/value chunk k, v [N_k, d].
+
+    Causal: query i may attend key j iff j <= i + diag (for the chunk [a, b) of a sequence
+    whose queries start at position q0, diag = q0 - a). Rows with no allowed key give O = 0
+    and LSE = -inf. The plain definition, as ``attention_head``.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    nq, nk = q.shape[0], k.shape[0]
+    if nq == 0:
+        return np.zeros((0, v.shape[1])), np.zeros((0,))
+    if nk == 0:
+        return np.zeros((nq, v.shape[1])), np.full((nq,), -np.inf)
+    s = float(scale) * (q @ k.T)
+    if causal:
+        s[np.arange(nk)[None, :] > np.arange(nq)[:, None] + int(diag)] = -np.inf
+    p, lse = _softmax_rows(s)
+    return p @ v, lse
+
+
+def attention_chunk(q, k, v, causal: bool, diag: int, scale: float):
+    """``attention_chunk_head`` over q [B, H, N_q, d] and k, v [B, H_kv, N_k, d]."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, nq, _ = q.shape
+    H_kv = k.shape[1]
+    o = np.zeros((B, H, nq, v.shape[3]))
+    lse = np.zeros((B, H, nq))
+    for b in range(B):
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            o[b, h], lse[b, h] = attention_chunk_head(q[b, h], k[b, hk], v[b, hk], causal, diag, scale)
+    return o, lse
+
+
+def lse_merge(o_parts, lse_parts):
+    """Merge partial results over disjoint key sets (llm-infra-atlas "FlashAttention" §5 and
+    the LSE mix of its §0 reading table): LSE = log sum_s exp(LSE_s),
+    O = sum_s exp(LSE_s - LSE) O_s. o_parts [S, ..., d], lse_parts [S, ...]; rows whose LSE_s
+    are all -inf give O = 0, LSE = -inf. Returns (O [..., d], LSE [...]) in float64."""
+    o_parts, lse_parts = _as_f64(o_parts), _as_f64(lse_parts)
+    m = lse_parts.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(lse_parts - m_safe[None])               # exp(-inf) = 0
+    z = w.sum(axis=0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        lse = np.where(z > 0, m_safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+        wn = np.where(z[None] > 0, w / np.where(z > 0, z, 1.0)[None], 0.0)
+    o = np.sum(wn[..., None] * o_parts, axis=0)
+    return o, lse

@@ -207,6 +207,66 @@ def test_bwd_empty_is_ok():
     assert _bwd_varlen(T=0, cu=None, **none) == 0
 
 
+def _chunk(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, H_kv=2, Nq=16, Nk=32, d=64, causal=1, diag=0,
+           scale=0.125, variant=0):
+    return fa2.load_library().fa2_fwd_chunk(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, causal, diag, scale, variant,
+                                            None)
+
+
+def _splitkv(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, H_kv=2, Nq=16, Nk=640, d=128, causal=1, diag=0,
+             scale=0.088, S=4, op=FAKE, lp=FAKE, variant=0):
+    return fa2.load_library().fa2_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, causal, diag, scale, S, op, lp,
+                                              variant, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(S=0), 2), (dict(S=-3), 2), (dict(op=None), 1), (dict(lp=None), 1), (dict(op=FAKE + 8), 4),
+    (dict(lp=FAKE + 1), 4), (dict(S=70000), 9), (dict(H_kv=3), 2), (dict(d=256), 3), (dict(variant=-2), 8),
+])
+def test_splitkv_validation(kwargs, code):
+    assert _splitkv(**kwargs) == code
+
+
+def test_splitkv_workspace_unused_without_split():
+    # One split, or no keys: the workspace is not needed; validation passes (then a device is needed).
+    assert _splitkv(S=1, op=None, lp=None) in (0, 6)
+    assert _splitkv(Nk=0, k=None, v=None, op=None, lp=None) in (0, 6)
+
+
+def _merge(op=FAKE, lp=FAKE, S=2, rows=100, d=128, o=FAKE, lse=FAKE):
+    return fa2.load_library().fa2_lse_merge(op, lp, S, rows, d, o, lse, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(Nq=-1), 2), (dict(Nk=-1), 2), (dict(H_kv=3), 2), (dict(diag=(1 << 30) + 1), 2),
+    (dict(diag=-(1 << 30) - 1), 2), (dict(q=None), 1), (dict(k=None), 1), (dict(d=80), 3),
+    (dict(o=FAKE + 2), 4), (dict(variant=50), 8), (dict(scale=float("nan")), 5),
+    (dict(B=1 << 10, H=1 << 10, Nq=1 << 12), 9),
+])
+def test_chunk_validation(kwargs, code):
+    assert _chunk(**kwargs) == code
+
+
+def test_chunk_empty_and_no_keys():
+    assert _chunk(Nq=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    # N_k == 0: k and v may be NULL; with valid q/o/lse the call passes validation and
+    # only then needs a device.
+    code = _chunk(Nk=0, k=None, v=None)
+    assert code in (0, 6)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(S=0), 2), (dict(rows=-1), 2), (dict(d=96), 3), (dict(op=None), 1), (dict(lse=None), 1),
+    (dict(op=FAKE + 8), 4), (dict(lp=FAKE + 2), 4), (dict(o=FAKE + 4), 4),
+])
+def test_merge_validation(kwargs, code):
+    assert _merge(**kwargs) == code
+
+
+def test_merge_empty_is_ok():
+    assert _merge(rows=0, op=None, lp=None, o=None, lse=None) == 0
+
+
 def _gpu_present():
     if os.path.exists("/dev/kfd"):
         return True
@@ -226,6 +286,9 @@ def test_no_device_reported():
     assert _varlen_gqa() == 6
     assert _bwd() == 6
     assert _bwd_varlen() == 6
+    assert _chunk() == 6
+    assert _merge() == 6
+    assert _splitkv() == 6
 
 
 def test_binding_rejects_cpu_tensors():
