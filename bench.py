@@ -104,6 +104,12 @@ def run(args):
     from synthetic import WORKLOADS, metric_flops, varlen_metric_flops, workload_inputs
 
     w = WORKLOADS[args.workload]
+    if args.head_dim:
+        import dataclasses
+        if w.varlen:
+            raise SystemExit("--head-dim applies to fixed-length workloads")
+        w = dataclasses.replace(w, d=args.head_dim,
+                                description=w.description.replace(f"d={w.d}", f"d={args.head_dim}"))
     dev = torch.device("cuda:0")
     lengths = None
     if w.varlen:
@@ -236,7 +242,8 @@ def run(args):
                                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
 
     traffic = None
-    t = (load_traffic() if (w.name == "c4" and args.variant == 0 and not (args.kv_heads or args.bwd or args.split_kv))
+    t = (load_traffic() if (w.name == "c4" and args.variant == 0
+                            and not (args.kv_heads or args.bwd or args.split_kv or args.head_dim))
          else None)
     if t is not None:
         traffic = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
@@ -267,7 +274,8 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3)
-                        if w.name == "c4" and not (args.kv_heads or args.bwd or args.split_kv) else None),
+                        if w.name == "c4" and not (args.kv_heads or args.bwd or args.split_kv or args.head_dim)
+                        else None),
         "dtype": "bf16",
         "data": "synthetic",
         "config": config,
@@ -287,7 +295,8 @@ def run(args):
     }
     if args.cpu_baseline_heads > 0:
         out["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_baseline_heads)
-                               if not (w.varlen or args.kv_heads or args.bwd or args.split_kv) else None)
+                               if not (w.varlen or args.kv_heads or args.bwd or args.split_kv or args.head_dim)
+                               else None)
     print(json.dumps(out), flush=True)
 
 
@@ -336,6 +345,8 @@ def main():
                     help="split the keys into this many pieces in one launch and merge them (fa2_fwd_splitkv)")
     ap.add_argument("--q-rows", type=int, default=0,
                     help="with --split-kv: only the last Q_ROWS queries (decode / chunked prefill shape)")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="override the workload's head dimension (64, 128 or 256)")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped-query attention: K/V with this many heads (must divide H; 0: H)")
     ap.add_argument("--cpu-baseline-heads", type=int, default=8,

@@ -98,15 +98,15 @@ struct Tile {
   static constexpr int NKC = D / 16;                // 16-wide contraction steps of QK^T
   static constexpr int NDB = D / 32;                // 32-wide d blocks of O^T
   static constexpr int NPC = BC / 16;               // 16-key contraction steps of PV
-  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
   static_assert(BC % 32 == 0 && TILEB % (1024 * WAVES) == 0, "tile shape");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
   // Swizzle of K rows: lanes reading 16 consecutive rows at one logical chunk land in 16
   // distinct 16-byte bank groups.
-  __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  __device__ static int kswz(int row) { return D >= 128 ? (row & 15) : ((row >> 1) & 7); }
   // Swizzle of V rows: a transposed read touches 4 consecutive rows x 2..4 chunks.
-  __device__ static int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
+  __device__ static int vswz(int row) { return D >= 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 };
 
 // Workgroup id -> (batch|sequence * H + head, row block). With the XCD-aware order,
@@ -151,7 +151,8 @@ constexpr float kOptLimit = 256.0f;   // 2^kLazyTau
 // LA: how many operand fragments are read from LDS ahead of the MFMA that consumes them
 // (0 leaves the order to the compiler's scheduler).
 template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
 void fa2_fwd_kernel(Params p) {
   using TL = Tile<D, BC>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
@@ -842,9 +843,19 @@ const Variant* variants_for(int d, int* count) {
       make_variant<128, 64, kLazy, 4>("d128_bc64_lazy_la4"),
       make_variant<128, 64, kExact>("d128_bc64_exact"),
       make_variant_pp<128, 64, 4>("d128_pp_bc64_la4")};
+  // d = 256: one wave per SIMD (the O~ accumulator alone is 128 registers), so the
+  // ping-pong family, which needs two waves per SIMD, has no d = 256 member.
+  static const Variant v256[] = {
+      make_variant<256, 64, kOptimistic, 4>("d256_bc64_opt_la4"),
+      make_variant<256, 32, kOptimistic, 4>("d256_bc32_opt_la4"),
+      make_variant<256, 64, kExact>("d256_bc64_exact")};
   if (d == 64) {
     *count = (int)(sizeof(v64) / sizeof(v64[0]));
     return v64;
+  }
+  if (d == 256) {
+    *count = (int)(sizeof(v256) / sizeof(v256[0]));
+    return v256;
   }
   if (d == 128) {
     *count = (int)(sizeof(v128) / sizeof(v128[0]));
@@ -856,10 +867,12 @@ const Variant* variants_for(int d, int* count) {
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
+bool fwd_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
 int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  int d, float scale, int variant, const Variant** out) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL_PTR;
-  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (!fwd_head_dim(d)) return FA2_ERR_UNSUPPORTED_HEADDIM;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA2_ERR_MISALIGNED;
   if (!isfinite(scale)) return FA2_ERR_BAD_SCALE;
@@ -900,7 +913,7 @@ int fwd_chunk_impl(const void* q, const void* k, const void* v, void* o, float* 
   if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N_q < 0 || N_k < 0)
     return FA2_ERR_BAD_SHAPE;
   if (diag < -(1 << 30) || diag > (1 << 30)) return FA2_ERR_BAD_SHAPE;
-  if (N_q == 0) return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (N_q == 0) return fwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   if (N_k == 0) k = v = q;   // never read: every row gets O = 0, LSE = -inf
   const Variant* var = nullptr;
   int st = check_common(q, k, v, o, lse, d, scale, variant, &var);
@@ -970,7 +983,7 @@ const char* fa2_status_str(int status) {
     case FA2_OK: return "ok";
     case FA2_ERR_NULL_PTR: return "a required pointer is NULL";
     case FA2_ERR_BAD_SHAPE: return "bad shape (B, H must be > 0, N >= 0; varlen sizes consistent)";
-    case FA2_ERR_UNSUPPORTED_HEADDIM: return "unsupported head dimension (64 or 128)";
+    case FA2_ERR_UNSUPPORTED_HEADDIM: return "unsupported head dimension (forward 64/128/256, backward 64/128)";
     case FA2_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 B, lse 4 B)";
     case FA2_ERR_BAD_SCALE: return "scale is not finite";
     case FA2_ERR_NO_DEVICE: return "no usable HIP device";
@@ -1038,7 +1051,7 @@ int fa2_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, flo
       total_tokens < 0)
     return FA2_ERR_BAD_SHAPE;
   if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
-    return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+    return fwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   if (!cu_seqlens) return FA2_ERR_NULL_PTR;
   if (!aligned(cu_seqlens, 4)) return FA2_ERR_MISALIGNED;
   const Variant* var = nullptr;

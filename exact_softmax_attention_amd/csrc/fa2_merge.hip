@@ -71,7 +71,7 @@ extern "C" {
 int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, long long rows,
                   int d, void* o, float* lse, void* stream) {
   if (num_parts <= 0 || rows < 0) return FA2_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEADDIM;
   if (rows == 0) return FA2_OK;
   if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL_PTR;
   if (!aligned16(o_parts) || !aligned16(o) || ((uintptr_t)lse_parts & 3) || ((uintptr_t)lse & 3))
@@ -81,7 +81,9 @@ int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, lo
   if (blocks > 0x7fffffffLL || (long long)num_parts * rows > (1LL << 40)) return FA2_ERR_TOO_LARGE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
-  const void* fn = d == 64 ? (const void*)&fa2_lse_merge_kernel<64> : (const void*)&fa2_lse_merge_kernel<128>;
+  const void* fn = d == 64    ? (const void*)&fa2_lse_merge_kernel<64>
+                   : d == 128 ? (const void*)&fa2_lse_merge_kernel<128>
+                              : (const void*)&fa2_lse_merge_kernel<256>;
   const uint16_t* op = (const uint16_t*)o_parts;
   uint16_t* oo = (uint16_t*)o;
   void* args[] = {&op, &lse_parts, &num_parts, &rows, &oo, &lse};

@@ -46,7 +46,7 @@ enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULL_PTR = 1,            /* a required pointer is NULL */
   FA2_ERR_BAD_SHAPE = 2,           /* B, H or H_kv <= 0, H_kv not dividing H, N < 0, ... */
-  FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* d is not 64 or 128 */
+  FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* d not 64/128/256 (forward, merge) or 64/128 (backward) */
   FA2_ERR_MISALIGNED = 4,          /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
   FA2_ERR_BAD_SCALE = 5,           /* scale is NaN or infinite */
   FA2_ERR_NO_DEVICE = 6,           /* no usable HIP device is current */
@@ -60,7 +60,7 @@ enum fa2_status {
  *   q, k, v : bf16 [B, H, N, d], contiguous (d fastest), read only.
  *   o       : bf16 [B, H, N, d], contiguous; written with round-to-nearest-even.
  *   lse     : fp32 [B, H, N]; natural-log logsumexp of each row of S.
- *   d       : 64 or 128.  causal: 0 or 1 (mask key j > query i).
+ *   d       : 64, 128 or 256.  causal: 0 or 1 (mask key j > query i).
  *   scale   : any finite float (typically 1/sqrt(d)); applied to QK^T before the softmax.
  * Returns FA2_OK or an error code (see above).
  */
@@ -166,7 +166,7 @@ int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float*
  *   lse_parts : fp32 [num_parts, rows] (natural log; -inf marks a row with no key in part s).
  *   o         : bf16 [rows, d]; lse : fp32 [rows]; written. rows is any count, e.g.
  *               B * H * N_q for fa2_fwd_chunk outputs. o/lse must not alias the parts.
- *   d         : 64 or 128.  num_parts >= 1.
+ *   d         : 64, 128 or 256.  num_parts >= 1.
  * A row whose LSE_s are all -inf gets O = 0 and LSE = -inf. rows == 0 succeeds without a
  * launch. Validation, ownership and asynchrony as for fa2_fwd.
  */
@@ -187,7 +187,8 @@ int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, lo
  *   lse            : fp32 [B, H, N], the forward's logsumexp (natural log);
  *   delta          : fp32 [B, H, N] caller-provided buffer, overwritten with D (it is the
  *                    only intermediate; the library allocates nothing).
- *   H_kv must divide H. d, causal and scale as for the forward (same scale as the forward).
+ *   H_kv must divide H. d is 64 or 128 (the forward's d = 256 has no backward yet); causal
+ *   and scale as for the forward (same scale as the forward).
  *   dq, dk, dv and delta are fully overwritten on success; they must not alias the inputs.
  * Two kernels run in order on stream (dQ and D, then dK and dV); no atomics are used, so the
  * gradients are bitwise reproducible. Validation, ownership and zero-size rules as fa2_fwd.

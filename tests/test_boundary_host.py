@@ -45,7 +45,7 @@ def test_abi_version_and_status_strings():
 
 
 def test_variants_listed():
-    for d in (64, 128):
+    for d in (64, 128, 256):
         n = fa2.num_variants(d)
         assert n >= 1
         names = [fa2.variant_name(d, i) for i in range(n)]
@@ -105,7 +105,7 @@ def _varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, S=2, maxlen=16, T
 @pytest.mark.parametrize("kwargs,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=-5), 2),
-    (dict(d=96), 3), (dict(d=256), 3), (dict(d=0), 3),
+    (dict(d=96), 3), (dict(d=512), 3), (dict(d=0), 3),
     (dict(q=FAKE + 8), 4), (dict(o=FAKE + 2), 4), (dict(lse=FAKE + 2), 4),
     (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5), (dict(scale=-float("inf")), 5),
     (dict(variant=-1), 8), (dict(variant=99), 8),
@@ -186,7 +186,7 @@ def _bwd_varlen(cu=FAKE, S=2, maxlen=16, T=32, H=4, H_kv=4, d=64, causal=0, scal
     (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1),
     (dict(dk=None), 1), (dict(dv=None), 1), (dict(delta=None), 1),
     (dict(B=0), 2), (dict(H_kv=3), 2), (dict(H_kv=0), 2), (dict(N=-1), 2),
-    (dict(d=96), 3), (dict(dq=FAKE + 8), 4), (dict(delta=FAKE + 2), 4), (dict(o=FAKE + 4), 4),
+    (dict(d=96), 3), (dict(d=256), 3), (dict(dq=FAKE + 8), 4), (dict(delta=FAKE + 2), 4), (dict(o=FAKE + 4), 4),
     (dict(scale=float("nan")), 5), (dict(N=1 << 30, H=64, H_kv=64), 9),
 ])
 def test_bwd_validation(kwargs, code):
@@ -221,7 +221,7 @@ def _splitkv(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, H_kv=2, Nq=16, 
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(S=0), 2), (dict(S=-3), 2), (dict(op=None), 1), (dict(lp=None), 1), (dict(op=FAKE + 8), 4),
-    (dict(lp=FAKE + 1), 4), (dict(S=70000), 9), (dict(H_kv=3), 2), (dict(d=256), 3), (dict(variant=-2), 8),
+    (dict(lp=FAKE + 1), 4), (dict(S=70000), 9), (dict(H_kv=3), 2), (dict(d=512), 3), (dict(variant=-2), 8),
 ])
 def test_splitkv_validation(kwargs, code):
     assert _splitkv(**kwargs) == code

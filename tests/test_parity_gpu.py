@@ -105,7 +105,7 @@ def test_c5_varlen_sampled():
 ODD_N = [1, 17, 100, 128, 129, 255, 1000]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", ODD_N)
 def test_odd_shapes_full(N, d, causal):
@@ -117,7 +117,7 @@ def test_odd_shapes_full(N, d, causal):
         _check(_f64(o), _f64(l), o_ref, l_ref, f"N{N} d{d} causal{int(causal)} {fa2.variant_name(d, variant)}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_edges_full(d, causal):
     lengths = [1, 127, 0, 128, 129, 5, 300, 64, 255, 256, 1000, 2]
@@ -161,7 +161,7 @@ def test_large_scores():
         _check(_f64(o), _f64(l), o_ref, l_ref, f"scores x16 causal{int(causal)}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_long_sequence_sampled(d):
     N = 65537
     q, k, v = make_qkv(1, 2, N, d, seed=33)

@@ -33,7 +33,7 @@ def _check(o_gpu, l_gpu, o_ref, l_ref, tag):
     assert mx <= O_MAX and mean <= O_MEAN and lmx <= LSE_MAX, tag
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("H,H_kv", [(8, 1), (8, 2), (6, 3), (8, 8)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_small(d, H, H_kv, causal):
@@ -48,7 +48,7 @@ def test_gqa_small(d, H, H_kv, causal):
         _check(_f64(o), _f64(l), o_ref, l_ref, f"gqa d{d} H{H}/{H_kv} causal={causal} v{variant}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_gqa_varlen(d):
     lengths = [1, 127, 0, 128, 129, 300, 64, 2]
     H, H_kv = 8, 2

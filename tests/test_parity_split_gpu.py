@@ -40,7 +40,7 @@ def _check(o, l, o_ref, l_ref, tag):
     assert mx <= O_MAX and mean <= O_MEAN and lmx <= LSE_MAX, tag
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("nq,nk", [(1, 300), (100, 1), (257, 1000), (300, 0), (129, 129), (64, 200)])
 def test_chunk_small(d, nq, nk):
     gen_q = make_qkv(1, 4, nq, d, seed=400 + nq + d)[0]
@@ -58,7 +58,7 @@ def test_chunk_small(d, nq, nk):
                 _check(_f64(o), _f64(l), o_ref, l_ref, f"chunk d{d} {nq}x{nk} causal={causal} diag={diag} v{variant}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_merge_kernel(d):
     gen = torch.Generator(device="cpu").manual_seed(600 + d)
     S, rows = 3, 1000
@@ -121,7 +121,7 @@ def test_split_kv_long_and_decode():
             _check(_f64(o[0, h, rows]), _f64(l[0, h, rows]), o_ref, l_ref, f"split-kv long nq={nq} h{h} vs oracle")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("nq,nk", [(1, 1000), (16, 5000), (257, 1000), (100, 1), (130, 0)])
 def test_splitkv_one_launch(d, nq, nk):
     q = make_qkv(1, 4, nq, d, seed=700 + nq + d)[0]
