@@ -37,14 +37,18 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PF)
 PEAK_HBM_GBS = 8000.0
 A100_FIG5D_16K_TFLOPS = 197.0   # the pages' FA2 forward, causal, d=128, 16k (A100; context only)
-KERNEL_SRC = os.path.join(ROOT, "exact_softmax_attention_amd", "csrc", "fa2_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "exact_softmax_attention_amd", "csrc", name) for name in ("fa2_fwd.hip", "fa2_dev.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_c4_traffic.json")
 COPY_BYTES = 1 << 30   # the calibration copy kernel moves 1 GiB in and 1 GiB out
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernel's sources (the kernel file and the device helpers it includes)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(w, lengths=None, kv_heads=None) -> int:
