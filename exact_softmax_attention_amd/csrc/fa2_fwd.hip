@@ -81,12 +81,14 @@ struct Params {
   uint32_t qflip;         // 0x80008000 negates Q (scale < 0), else 0
 };
 
-// Compile-time tile geometry. K and V tiles are BC rows of D bf16 (row pitch 2*D bytes,
-// no padding), stored in LDS with their 16-byte chunks permuted by an XOR of low row bits
-// so that the MFMA operand reads below hit distinct banks.
-template <int D, int BC>
+// Compile-time tile geometry. NW waves of 32 query rows share each K/V tile (NW = 8 puts
+// one 256-row workgroup on a CU, two waves per SIMD, and halves the K/V staging per query
+// row against NW = 4). K and V tiles are BC rows of D bf16 (row pitch 2*D bytes, no
+// padding), stored in LDS with their 16-byte chunks permuted by an XOR of low row bits so
+// that the MFMA operand reads below hit distinct banks.
+template <int D, int BC, int NW = 4>
 struct Tile {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = NW;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;             // query rows per workgroup
   static constexpr int ROWB = 2 * D;                // bytes per K or V row
@@ -150,11 +152,11 @@ constexpr float kOptLimit = 256.0f;   // 2^kLazyTau
 
 // LA: how many operand fragments are read from LDS ahead of the MFMA that consumes them
 // (0 leaves the order to the compiler's scheduler).
-template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW = 4>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
 void fa2_fwd_kernel(Params p) {
-  using TL = Tile<D, BC>;
+  using TL = Tile<D, BC, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
 
@@ -795,9 +797,9 @@ struct Variant {
   KernelFn varlen[2];  // [causal]
 };
 
-template <int D, int BC, int MODE, int LA = 0>
+template <int D, int BC, int MODE, int LA = 0, int NW = 4>
 Variant make_variant(const char* name) {
-  using TL = Tile<D, BC>;
+  using TL = Tile<D, BC, NW>;
   Variant v;
   v.threads = TL::THREADS;
   v.name = name;
@@ -805,10 +807,10 @@ Variant make_variant(const char* name) {
   v.br = TL::BR;
   v.bc = BC;
   v.lds = TL::LDS_BYTES;
-  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false, MODE, LA>;
-  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false, MODE, LA>;
-  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true, MODE, LA>;
-  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true, MODE, LA>;
+  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false, MODE, LA, NW>;
+  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false, MODE, LA, NW>;
+  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true, MODE, LA, NW>;
+  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true, MODE, LA, NW>;
   return v;
 }
 
@@ -836,8 +838,10 @@ const Variant* variants_for(int d, int* count) {
       make_variant<64, 128, kOptimistic>("d64_bc128_opt"),
       make_variant<64, 128, kLazy, 4>("d64_bc128_lazy_la4"),
       make_variant<64, 128, kExact>("d64_bc128_exact"),
-      make_variant_pp<64, 64, 4>("d64_pp_bc64_la4")};
+      make_variant_pp<64, 64, 4>("d64_pp_bc64_la4"),
+      make_variant<64, 128, kOptimistic, 4, 8>("d64_w8_bc128_opt_la4")};
   static const Variant v128[] = {
+      make_variant<128, 64, kOptimistic, 4, 8>("d128_w8_bc64_opt_la4"),
       make_variant<128, 64, kOptimistic, 4>("d128_bc64_opt_la4"),
       make_variant<128, 64, kOptimistic>("d128_bc64_opt"),
       make_variant<128, 64, kLazy, 4>("d128_bc64_lazy_la4"),
