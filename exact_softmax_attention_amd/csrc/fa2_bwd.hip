@@ -142,9 +142,9 @@ __device__ __forceinline__ size_t kv_plane(const BwdParams& p, int bi, int hk) {
 
 // ---- dQ kernel -------------------------------------------------------------------------
 
-template <int D, int BC>
+template <int D, int BC, int NW = 4>
 struct DqTile {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = NW;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;
   static constexpr int ROWB = 2 * D;
@@ -160,10 +160,10 @@ struct DqTile {
   static_assert(BC % 32 == 0 && DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
 };
 
-template <int D, int BC, bool CAUSAL, bool VARLEN>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <int D, int BC, bool CAUSAL, bool VARLEN, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dq_kernel(BwdParams p) {
-  using TL = DqTile<D, BC>;
+  using TL = DqTile<D, BC, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
 
@@ -599,22 +599,24 @@ typedef const void* KernelFn;
 
 struct BwdKernels {
   int dq_bc;
+  int dq_br;
   int dq_threads;
   int dkdv_threads;
   KernelFn dq[2][2];     // [varlen][causal]
   KernelFn dkdv[2][2];
 };
 
-template <int D, int BC_DQ, int OCC_DKDV>
+template <int D, int BC_DQ, int NW_DQ, int OCC_DKDV>
 BwdKernels make_bwd() {
   BwdKernels k;
   k.dq_bc = BC_DQ;
-  k.dq_threads = DqTile<D, BC_DQ>::THREADS;
+  k.dq_br = DqTile<D, BC_DQ, NW_DQ>::BR;
+  k.dq_threads = DqTile<D, BC_DQ, NW_DQ>::THREADS;
   k.dkdv_threads = DkvTile<D, 64>::THREADS;
-  k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false>;
-  k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false>;
-  k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true>;
-  k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true>;
+  k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false, NW_DQ>;
+  k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false, NW_DQ>;
+  k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true, NW_DQ>;
+  k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true, NW_DQ>;
   k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, false, false, OCC_DKDV>;
   k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, true, false, OCC_DKDV>;
   k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, false, true, OCC_DKDV>;
@@ -623,8 +625,8 @@ BwdKernels make_bwd() {
 }
 
 const BwdKernels* bwd_kernels(int d) {
-  static const BwdKernels k64 = make_bwd<64, 64, 2>();
-  static const BwdKernels k128 = make_bwd<128, 32, 1>();
+  static const BwdKernels k64 = make_bwd<64, 64, 4, 2>();
+  static const BwdKernels k128 = make_bwd<128, 32, 4, 1>();
   return d == 64 ? &k64 : d == 128 ? &k128 : nullptr;
 }
 
@@ -704,7 +706,9 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.g = H / H_kv;
   p.N = N;
   p.T = N;
-  return bwd_launch(*bwd_kernels(d), false, causal != 0, p, (int)nblk, (int)nblk, pq, pk, stream);
+  const BwdKernels& kk = *bwd_kernels(d);
+  const long long nblk_q = ((long long)N + kk.dq_br - 1) / kk.dq_br;
+  return bwd_launch(kk, false, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
 }
 
 int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -731,7 +735,9 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   p.g = H / H_kv;
   p.N = max_seqlen;
   p.T = total_tokens;
-  return bwd_launch(*bwd_kernels(d), true, causal != 0, p, (int)nblk, (int)nblk, pq, pk, stream);
+  const BwdKernels& kk = *bwd_kernels(d);
+  const long long nblk_q = ((long long)max_seqlen + kk.dq_br - 1) / kk.dq_br;
+  return bwd_launch(kk, true, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
 }
 
 }  // extern "C"
