@@ -66,6 +66,9 @@ struct Params {
   float* lse;
   const int* cu_seqlens;  // varlen only
   int nb;                 // batch size, or number of sequences (varlen)
+  int dg;                 // head dimension of the tensors (a multiple of 8, <= D; the kernel's
+                          // D is the next of 64 / 128 / 256 and the extra columns are zero
+                          // in Q and never written in O)
   int H;                  // query heads
   int Hkv;                // key/value heads (H for MHA)
   int g;                  // query heads per key/value head, H / Hkv
@@ -204,9 +207,11 @@ void fa2_fwd_kernel(Params p) {
   const int q0 = i * TL::BR;
   if (q0 >= seq_len) return;  // uniform over the workgroup (varlen rows past the end)
 
-  const uint16_t* __restrict__ qh = p.q + row0 * D;
-  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
-  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
+  const int dg = p.dg;            // row pitch of Q, K, V, O in elements
+  const int growb = 2 * dg;       // ... in bytes
+  const uint16_t* __restrict__ qh = p.q + row0 * dg;
+  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * dg);
+  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * dg);
 
   // Key tiles to visit: causal stops after the tile holding the last key this block's last
   // query may attend (none when the whole key range lies after it).
@@ -220,7 +225,7 @@ void fa2_fwd_kernel(Params p) {
 #pragma unroll
   for (int kc = 0; kc < TL::NKC; ++kc) {
     u32x4 t = {0u, 0u, 0u, 0u};
-    if (qrow < seq_len) t = *(const u32x4*)(qh + (size_t)qrow * D + kc * 16 + hl * 8);
+    if (qrow < seq_len && kc * 16 + hl * 8 < dg) t = *(const u32x4*)(qh + (size_t)qrow * dg + kc * 16 + hl * 8);
     t ^= p.qflip;
     qf[kc] = as_bf16x8(t);
   }
@@ -239,14 +244,16 @@ void fa2_fwd_kernel(Params p) {
     const int r = o / TL::ROWB;
     const int pch = (o % TL::ROWB) / 16;
     drow[d] = r;
-    koff[d] = r * TL::ROWB + ((pch ^ TL::kswz(r)) * 16);
-    voff[d] = r * TL::ROWB + ((pch ^ TL::vswz(r)) * 16);
+    // Padded columns (logical chunk beyond dg) load a real chunk of the same row: finite, and
+    // multiplied by Q's zero columns (K) or landing in unwritten O columns (V).
+    koff[d] = r * growb + (((pch ^ TL::kswz(r)) % (dg / 8)) * 16);
+    voff[d] = r * growb + (((pch ^ TL::vswz(r)) % (dg / 8)) * 16);
   }
 
   auto dma_tile = [&](int j, unsigned char* stage) {
     const int key0 = j * BC;
-    const unsigned char* kt = kh + (size_t)key0 * TL::ROWB;
-    const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
+    const unsigned char* kt = kh + (size_t)key0 * growb;
+    const unsigned char* vt = vh + (size_t)key0 * growb;
     const uint32_t ks_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
     const uint32_t vs_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
     if (key0 + BC <= seq_k) {
@@ -261,7 +268,7 @@ void fa2_fwd_kernel(Params p) {
       const int last = seq_k - 1 - key0;
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
-        const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * TL::ROWB;
+        const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * growb;
         dma16(kt, koff[d] - back, ks_a + d * 1024);
         dma16(vt, voff[d] - back, vs_a + d * 1024);
       }
@@ -451,14 +458,14 @@ void fa2_fwd_kernel(Params p) {
   const float l_tot = halves_sum(l_run);
   if (qrow < seq_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = p.o + (orow0 + (size_t)qrow) * D;
+    uint16_t* orow = p.o + (orow0 + (size_t)qrow) * dg;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
                    pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
+        if (db * 32 + 8 * g + 4 * hl < dg) *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
       }
     if (hl == 0) {
       p.lse[orow0 + (size_t)qrow] =
@@ -551,9 +558,11 @@ void fa2_fwd_kernel_pp(Params p) {
   const int q0 = i * TL::BR;
   if (q0 >= seq_len) return;
 
-  const uint16_t* __restrict__ qh = p.q + row0 * D;
-  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
-  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
+  const int dg = p.dg;            // row pitch of Q, K, V, O in elements
+  const int growb = 2 * dg;       // ... in bytes
+  const uint16_t* __restrict__ qh = p.q + row0 * dg;
+  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * dg);
+  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * dg);
   const int kv_end = max(CAUSAL ? min(seq_k, q0 + TL::BR + diag) : seq_k, 0);
   const int nt = (kv_end + BC - 1) / BC;
 
@@ -569,7 +578,7 @@ void fa2_fwd_kernel_pp(Params p) {
 #pragma unroll
   for (int kc = 0; kc < TL::NKC; ++kc) {
     u32x4 t = {0u, 0u, 0u, 0u};
-    if (qrow < seq_len) t = *(const u32x4*)(qh + (size_t)qrow * D + kc * 16 + hl * 8);
+    if (qrow < seq_len && kc * 16 + hl * 8 < dg) t = *(const u32x4*)(qh + (size_t)qrow * dg + kc * 16 + hl * 8);
     t ^= p.qflip;
     qf[kc] = as_bf16x8(t);
   }
@@ -585,14 +594,16 @@ void fa2_fwd_kernel_pp(Params p) {
     const int r = o / TL::ROWB;
     const int pch = (o % TL::ROWB) / 16;
     drow[d] = r;
-    koff[d] = r * TL::ROWB + ((pch ^ TL::kswz(r)) * 16);
-    voff[d] = r * TL::ROWB + ((pch ^ TL::vswz(r)) * 16);
+    // Padded columns (logical chunk beyond dg) load a real chunk of the same row: finite, and
+    // multiplied by Q's zero columns (K) or landing in unwritten O columns (V).
+    koff[d] = r * growb + (((pch ^ TL::kswz(r)) % (dg / 8)) * 16);
+    voff[d] = r * growb + (((pch ^ TL::vswz(r)) % (dg / 8)) * 16);
   }
   const uint32_t lds_base = lds_addr(lds);
   auto dma_tile = [&](int j) {
     const int key0 = j * BC;
-    const unsigned char* kt = kh + (size_t)key0 * TL::ROWB;
-    const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
+    const unsigned char* kt = kh + (size_t)key0 * growb;
+    const unsigned char* vt = vh + (size_t)key0 * growb;
     const uint32_t st = lds_base + (uint32_t)(j & (TL::NSTAGE - 1)) * TL::STAGEB;
     const uint32_t ks_a = st + wave * TL::DMA_PER_WAVE * 1024;
     const uint32_t vs_a = st + TL::TILEB + wave * TL::DMA_PER_WAVE * 1024;
@@ -606,7 +617,7 @@ void fa2_fwd_kernel_pp(Params p) {
       const int last = seq_k - 1 - key0;   // rows past the end re-read the last valid row
 #pragma unroll
       for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
-        const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * TL::ROWB;
+        const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * growb;
         dma16(kt, koff[d] - back, ks_a + d * 1024);
         dma16(vt, voff[d] - back, vs_a + d * 1024);
       }
@@ -766,14 +777,14 @@ void fa2_fwd_kernel_pp(Params p) {
   const float l_tot = halves_sum(l_run);
   if (qrow < seq_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = p.o + (orow0 + (size_t)qrow) * D;
+    uint16_t* orow = p.o + (orow0 + (size_t)qrow) * dg;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
                    pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
+        if (db * 32 + 8 * g + 4 * hl < dg) *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
       }
     if (hl == 0) {
       p.lse[orow0 + (size_t)qrow] =
@@ -871,7 +882,11 @@ const Variant* variants_for(int d, int* count) {
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
-bool fwd_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+// Head dimensions the forward accepts: any multiple of 8 up to 256. The kernels exist for
+// D = 64, 128 and 256; a smaller d runs on the next one with its columns padded (zero in Q,
+// unwritten in O), so its matrix work is that of the padded width.
+bool fwd_head_dim(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
+int padded_dim(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
 
 int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  int d, float scale, int variant, const Variant** out) {
@@ -881,7 +896,7 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
     return FA2_ERR_MISALIGNED;
   if (!isfinite(scale)) return FA2_ERR_BAD_SCALE;
   int count = 0;
-  const Variant* vs = variants_for(d, &count);
+  const Variant* vs = variants_for(padded_dim(d), &count);
   if (variant < 0 || variant >= count) return FA2_ERR_BAD_VARIANT;
   *out = &vs[variant];
   return FA2_OK;
@@ -946,6 +961,7 @@ int fwd_chunk_impl(const void* q, const void* k, const void* v, void* o, float* 
   p.lse = ns > 1 ? lse_parts : lse;
   p.cu_seqlens = nullptr;
   p.nb = B;
+  p.dg = d;
   p.H = H;
   p.Hkv = H_kv;
   p.g = H / H_kv;
@@ -971,14 +987,14 @@ int fa2_abi_version(void) { return FA2_ABI_VERSION; }
 
 int fa2_num_variants(int d) {
   int count = 0;
-  variants_for(d, &count);
+  if (fwd_head_dim(d)) variants_for(padded_dim(d), &count);
   return count;
 }
 
 const char* fa2_variant_name(int d, int variant) {
   int count = 0;
-  const Variant* vs = variants_for(d, &count);
-  if (variant < 0 || variant >= count) return "";
+  const Variant* vs = fwd_head_dim(d) ? variants_for(padded_dim(d), &count) : nullptr;
+  if (!vs || variant < 0 || variant >= count) return "";
   return vs[variant].name;
 }
 
@@ -987,7 +1003,8 @@ const char* fa2_status_str(int status) {
     case FA2_OK: return "ok";
     case FA2_ERR_NULL_PTR: return "a required pointer is NULL";
     case FA2_ERR_BAD_SHAPE: return "bad shape (B, H must be > 0, N >= 0; varlen sizes consistent)";
-    case FA2_ERR_UNSUPPORTED_HEADDIM: return "unsupported head dimension (forward 64/128/256, backward 64/128)";
+    case FA2_ERR_UNSUPPORTED_HEADDIM:
+      return "unsupported head dimension (forward: multiple of 8 up to 256; backward: 64 or 128)";
     case FA2_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 B, lse 4 B)";
     case FA2_ERR_BAD_SCALE: return "scale is not finite";
     case FA2_ERR_NO_DEVICE: return "no usable HIP device";
@@ -1003,7 +1020,7 @@ int fa2_fwd_geometry(int B, int H, int N, int d, int causal, int variant, int* n
   (void)causal;
   if (B <= 0 || H <= 0 || N < 0) return FA2_ERR_BAD_SHAPE;
   int count = 0;
-  const Variant* vs = variants_for(d, &count);
+  const Variant* vs = fwd_head_dim(d) ? variants_for(padded_dim(d), &count) : nullptr;
   if (!vs) return FA2_ERR_UNSUPPORTED_HEADDIM;
   if (variant < 0 || variant >= count) return FA2_ERR_BAD_VARIANT;
   const Variant& var = vs[variant];
@@ -1073,6 +1090,7 @@ int fa2_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, flo
   p.lse = lse;
   p.cu_seqlens = cu_seqlens;
   p.nb = num_seqs;
+  p.dg = d;
   p.H = H;
   p.Hkv = H_kv;
   p.g = H / H_kv;

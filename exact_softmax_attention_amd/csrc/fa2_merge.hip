@@ -26,10 +26,12 @@
 
 namespace {
 
+// D: 64, 128 or 256, at least the tensors' head dimension dg (a multiple of 8); lanes past
+// dg / 8 only compute the row's weights.
 template <int D>
 __global__ __launch_bounds__(256) void fa2_lse_merge_kernel(const uint16_t* __restrict__ o_parts,
                                                             const float* __restrict__ lse_parts,
-                                                            int num_parts, long long rows,
+                                                            int num_parts, long long rows, int dg,
                                                             uint16_t* __restrict__ o,
                                                             float* __restrict__ lse) {
   constexpr int LPR = D / 8;          // lanes per row
@@ -37,6 +39,7 @@ __global__ __launch_bounds__(256) void fa2_lse_merge_kernel(const uint16_t* __re
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
   if (row >= rows) return;
+  const bool has_cols = part * 8 < dg;
 
   float m = -INFINITY;
   for (int s = 0; s < num_parts; ++s) m = fmaxf(m, lse_parts[(size_t)s * rows + row]);
@@ -46,7 +49,8 @@ __global__ __launch_bounds__(256) void fa2_lse_merge_kernel(const uint16_t* __re
   if (m != -INFINITY) {
     for (int s = 0; s < num_parts; ++s) {
       const float w = __builtin_amdgcn_exp2f((lse_parts[(size_t)s * rows + row] - m) * kLog2e);
-      const u32x4 t = *(const u32x4*)(o_parts + ((size_t)s * rows + row) * D + part * 8);
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (has_cols) t = *(const u32x4*)(o_parts + ((size_t)s * rows + row) * dg + part * 8);
       z += w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256) void fa2_lse_merge_kernel(const uint16_t* __re
   const float inv = z > 0.f ? 1.f / z : 0.f;
   const u32x4 out = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-  *(u32x4*)(o + (size_t)row * D + part * 8) = out;
+  if (has_cols) *(u32x4*)(o + (size_t)row * dg + part * 8) = out;
   if (part == 0) lse[row] = z > 0.f ? m + __builtin_amdgcn_logf(z) * kLn2 : -INFINITY;
 }
 
@@ -71,22 +75,23 @@ extern "C" {
 int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, long long rows,
                   int d, void* o, float* lse, void* stream) {
   if (num_parts <= 0 || rows < 0) return FA2_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (d < 8 || d > 256 || d % 8 != 0) return FA2_ERR_UNSUPPORTED_HEADDIM;
   if (rows == 0) return FA2_OK;
   if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL_PTR;
   if (!aligned16(o_parts) || !aligned16(o) || ((uintptr_t)lse_parts & 3) || ((uintptr_t)lse & 3))
     return FA2_ERR_MISALIGNED;
-  const int rpb = 256 / (d / 8);
+  const int dpad = d <= 64 ? 64 : d <= 128 ? 128 : 256;
+  const int rpb = 256 / (dpad / 8);
   const long long blocks = (rows + rpb - 1) / rpb;
   if (blocks > 0x7fffffffLL || (long long)num_parts * rows > (1LL << 40)) return FA2_ERR_TOO_LARGE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
-  const void* fn = d == 64    ? (const void*)&fa2_lse_merge_kernel<64>
-                   : d == 128 ? (const void*)&fa2_lse_merge_kernel<128>
-                              : (const void*)&fa2_lse_merge_kernel<256>;
+  const void* fn = dpad == 64    ? (const void*)&fa2_lse_merge_kernel<64>
+                   : dpad == 128 ? (const void*)&fa2_lse_merge_kernel<128>
+                                 : (const void*)&fa2_lse_merge_kernel<256>;
   const uint16_t* op = (const uint16_t*)o_parts;
   uint16_t* oo = (uint16_t*)o;
-  void* args[] = {&op, &lse_parts, &num_parts, &rows, &oo, &lse};
+  void* args[] = {&op, &lse_parts, &num_parts, &rows, &d, &oo, &lse};
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }

@@ -46,7 +46,8 @@ enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULL_PTR = 1,            /* a required pointer is NULL */
   FA2_ERR_BAD_SHAPE = 2,           /* B, H or H_kv <= 0, H_kv not dividing H, N < 0, ... */
-  FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* d not 64/128/256 (forward, merge) or 64/128 (backward) */
+  FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* forward, merge: d not a multiple of 8 in [8, 256];
+                                      backward: d not 64 or 128 */
   FA2_ERR_MISALIGNED = 4,          /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
   FA2_ERR_BAD_SCALE = 5,           /* scale is NaN or infinite */
   FA2_ERR_NO_DEVICE = 6,           /* no usable HIP device is current */
@@ -60,7 +61,9 @@ enum fa2_status {
  *   q, k, v : bf16 [B, H, N, d], contiguous (d fastest), read only.
  *   o       : bf16 [B, H, N, d], contiguous; written with round-to-nearest-even.
  *   lse     : fp32 [B, H, N]; natural-log logsumexp of each row of S.
- *   d       : 64, 128 or 256.  causal: 0 or 1 (mask key j > query i).
+ *   d       : any multiple of 8 from 8 to 256 (64, 128 and 256 run natively; other
+ *             values run on the next of those widths with the extra columns padded, at the
+ *             padded width's matrix cost).  causal: 0 or 1 (mask key j > query i).
  *   scale   : any finite float (typically 1/sqrt(d)); applied to QK^T before the softmax.
  * Returns FA2_OK or an error code (see above).
  */
@@ -166,7 +169,7 @@ int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float*
  *   lse_parts : fp32 [num_parts, rows] (natural log; -inf marks a row with no key in part s).
  *   o         : bf16 [rows, d]; lse : fp32 [rows]; written. rows is any count, e.g.
  *               B * H * N_q for fa2_fwd_chunk outputs. o/lse must not alias the parts.
- *   d         : 64, 128 or 256.  num_parts >= 1.
+ *   d         : a multiple of 8 from 8 to 256.  num_parts >= 1.
  * A row whose LSE_s are all -inf gets O = 0 and LSE = -inf. rows == 0 succeeds without a
  * launch. Validation, ownership and asynchrony as for fa2_fwd.
  */
@@ -203,7 +206,8 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
                    const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
                    int H, int H_kv, int d, int causal, float scale, void* stream);
 
-/* Number of kernel variants for head dimension d (0 if d is unsupported). Host only. */
+/* Number of kernel variants for head dimension d (0 if d is unsupported; a padded d has
+ * the variants of its padded width). Host only. */
 int fa2_num_variants(int d);
 
 /*

@@ -45,13 +45,17 @@ def test_abi_version_and_status_strings():
 
 
 def test_variants_listed():
+    # A head dim that is not 64/128/256 runs on the next kernel width: same variants.
+    for d, dpad in ((8, 64), (96, 128), (192, 256)):
+        assert [fa2.variant_name(d, i) for i in range(fa2.num_variants(d))] == \
+            [fa2.variant_name(dpad, i) for i in range(fa2.num_variants(dpad))]
     for d in (64, 128, 256):
         n = fa2.num_variants(d)
         assert n >= 1
         names = [fa2.variant_name(d, i) for i in range(n)]
         assert all(names) and len(set(names)) == n
         assert fa2.variant_name(d, n) == ""
-    assert fa2.num_variants(96) == 0
+    assert fa2.num_variants(100) == 0
 
 
 def test_geometry_matches_worked_example():
@@ -80,7 +84,7 @@ def test_geometry_matches_worked_example():
 
 def test_geometry_errors():
     assert fa2.geometry(1, 1, 0, 64)["num_workgroups"] == 0
-    for args, code in (((0, 1, 8, 64), 2), ((1, 0, 8, 64), 2), ((1, 1, -1, 64), 2), ((1, 1, 8, 96), 3)):
+    for args, code in (((0, 1, 8, 64), 2), ((1, 0, 8, 64), 2), ((1, 1, -1, 64), 2), ((1, 1, 8, 100), 3)):
         with pytest.raises(fa2.Fa2Error) as e:
             fa2.geometry(*args)
         assert e.value.status == code
@@ -105,7 +109,7 @@ def _varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, S=2, maxlen=16, T
 @pytest.mark.parametrize("kwargs,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=-5), 2),
-    (dict(d=96), 3), (dict(d=512), 3), (dict(d=0), 3),
+    (dict(d=100), 3), (dict(d=264), 3), (dict(d=512), 3), (dict(d=0), 3), (dict(d=4), 3),
     (dict(q=FAKE + 8), 4), (dict(o=FAKE + 2), 4), (dict(lse=FAKE + 2), 4),
     (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5), (dict(scale=-float("inf")), 5),
     (dict(variant=-1), 8), (dict(variant=99), 8),
@@ -117,13 +121,13 @@ def test_fwd_validation(kwargs, code):
 
 def test_fwd_empty_is_ok_without_pointers():
     assert _fwd(q=None, k=None, v=None, o=None, lse=None, N=0) == 0
-    assert _fwd(q=None, k=None, v=None, o=None, lse=None, N=0, d=96) == 3
+    assert _fwd(q=None, k=None, v=None, o=None, lse=None, N=0, d=100) == 3
 
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(cu=None), 1), (dict(q=None), 1), (dict(lse=None), 1),
     (dict(H=0), 2), (dict(S=-1), 2), (dict(maxlen=-1), 2), (dict(T=-1), 2),
-    (dict(d=80), 3), (dict(cu=FAKE + 2), 4), (dict(k=FAKE + 4), 4),
+    (dict(d=84), 3), (dict(cu=FAKE + 2), 4), (dict(k=FAKE + 4), 4),
     (dict(scale=float("nan")), 5), (dict(variant=999), 8),
     (dict(S=1 << 20, maxlen=1 << 20, T=1 << 20, H=64), 9),
 ])
@@ -149,7 +153,7 @@ def _varlen_gqa(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, S=2, maxlen=1
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(H_kv=0), 2), (dict(H_kv=-2), 2), (dict(H_kv=3), 2), (dict(H_kv=16), 2), (dict(H=0), 2),
-    (dict(k=None), 1), (dict(v=FAKE + 4), 4), (dict(d=32), 3), (dict(variant=77), 8),
+    (dict(k=None), 1), (dict(v=FAKE + 4), 4), (dict(d=36), 3), (dict(variant=77), 8),
     (dict(scale=float("nan")), 5),
 ])
 def test_gqa_validation(kwargs, code):
@@ -157,7 +161,7 @@ def test_gqa_validation(kwargs, code):
 
 
 @pytest.mark.parametrize("kwargs,code", [
-    (dict(H_kv=0), 2), (dict(H_kv=3), 2), (dict(cu=None), 1), (dict(d=96), 3), (dict(variant=-1), 8),
+    (dict(H_kv=0), 2), (dict(H_kv=3), 2), (dict(cu=None), 1), (dict(d=97), 3), (dict(variant=-1), 8),
 ])
 def test_varlen_gqa_validation(kwargs, code):
     assert _varlen_gqa(**kwargs) == code
@@ -239,7 +243,7 @@ def _merge(op=FAKE, lp=FAKE, S=2, rows=100, d=128, o=FAKE, lse=FAKE):
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(Nq=-1), 2), (dict(Nk=-1), 2), (dict(H_kv=3), 2), (dict(diag=(1 << 30) + 1), 2),
-    (dict(diag=-(1 << 30) - 1), 2), (dict(q=None), 1), (dict(k=None), 1), (dict(d=80), 3),
+    (dict(diag=-(1 << 30) - 1), 2), (dict(q=None), 1), (dict(k=None), 1), (dict(d=81), 3),
     (dict(o=FAKE + 2), 4), (dict(variant=50), 8), (dict(scale=float("nan")), 5),
     (dict(B=1 << 10, H=1 << 10, Nq=1 << 12), 9),
 ])
@@ -256,7 +260,7 @@ def test_chunk_empty_and_no_keys():
 
 
 @pytest.mark.parametrize("kwargs,code", [
-    (dict(S=0), 2), (dict(rows=-1), 2), (dict(d=96), 3), (dict(op=None), 1), (dict(lse=None), 1),
+    (dict(S=0), 2), (dict(rows=-1), 2), (dict(d=100), 3), (dict(op=None), 1), (dict(lse=None), 1),
     (dict(op=FAKE + 8), 4), (dict(lp=FAKE + 2), 4), (dict(o=FAKE + 4), 4),
 ])
 def test_merge_validation(kwargs, code):

@@ -117,7 +117,20 @@ def test_odd_shapes_full(N, d, causal):
         _check(_f64(o), _f64(l), o_ref, l_ref, f"N{N} d{d} causal{int(causal)} {fa2.variant_name(d, variant)}")
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [8, 32, 80, 96, 160, 192, 248])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_not_64_128_256(d, causal):
+    """Head dims that are multiples of 8 run on the next kernel width with padded columns."""
+    for N in (1, 129, 300):
+        q, k, v = make_qkv(2, 3, N, d, seed=2000 + N + d + int(causal))
+        scale = 1.0 / math.sqrt(d)
+        o_ref, l_ref = attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
+        for variant in range(fa2.num_variants(d)):
+            o, l = _run_fixed(q, k, v, causal, scale, variant)
+            _check(_f64(o), _f64(l), o_ref, l_ref, f"N{N} d{d} causal{int(causal)} {fa2.variant_name(d, variant)}")
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_edges_full(d, causal):
     lengths = [1, 127, 0, 128, 129, 5, 300, 64, 255, 256, 1000, 2]

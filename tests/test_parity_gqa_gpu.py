@@ -33,7 +33,7 @@ def _check(o_gpu, l_gpu, o_ref, l_ref, tag):
     assert mx <= O_MAX and mean <= O_MEAN and lmx <= LSE_MAX, tag
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 80, 128, 256])
 @pytest.mark.parametrize("H,H_kv", [(8, 1), (8, 2), (6, 3), (8, 8)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_small(d, H, H_kv, causal):

@@ -58,7 +58,7 @@ def test_chunk_small(d, nq, nk):
                 _check(_f64(o), _f64(l), o_ref, l_ref, f"chunk d{d} {nq}x{nk} causal={causal} diag={diag} v{variant}")
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [40, 64, 96, 128, 192, 256])
 def test_merge_kernel(d):
     gen = torch.Generator(device="cpu").manual_seed(600 + d)
     S, rows = 3, 1000
@@ -121,7 +121,7 @@ def test_split_kv_long_and_decode():
             _check(_f64(o[0, h, rows]), _f64(l[0, h, rows]), o_ref, l_ref, f"split-kv long nq={nq} h{h} vs oracle")
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("nq,nk", [(1, 1000), (16, 5000), (257, 1000), (100, 1), (130, 0)])
 def test_splitkv_one_launch(d, nq, nk):
     q = make_qkv(1, 4, nq, d, seed=700 + nq + d)[0]
@@ -165,7 +165,7 @@ def test_splitkv_long_decode():
 
 
 def test_merge_rejects_bad_arguments():
-    o = torch.zeros((2, 10, 96), dtype=torch.bfloat16, device=DEV)
+    o = torch.zeros((2, 10, 100), dtype=torch.bfloat16, device=DEV)
     l = torch.zeros((2, 10), device=DEV)
     with pytest.raises(fa2.Fa2Error) as e:
         fa2.lse_merge(o, l)
