@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: exact softmax attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_16k_causal]
 
 One step = one forward over the whole batch of the workload (all of the hot path runs in
 one kernel launch). The default workload is the long-context causal one, B=1 H=16 N=16384
@@ -38,7 +38,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0
 A100_FIG5D_16K_TFLOPS = 197.0   # the pages' FA2 forward, causal, d=128, 16k (A100; context only)
 KERNEL_SRCS = [os.path.join(ROOT, "exact_softmax_attention_amd", "csrc", name) for name in ("fa2_fwd.hip", "fa2_dev.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_c4_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_long16k_traffic.json")
+WORKLOAD_NAMES = ("single_head_256", "batch8_2k_d128", "batch8_2k_d64_causal", "long_16k_causal", "varlen16_causal")
 COPY_BYTES = 1 << 30   # the calibration copy kernel moves 1 GiB in and 1 GiB out
 
 
@@ -246,7 +247,7 @@ def run(args):
                                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
 
     traffic = None
-    t = (load_traffic() if (w.name == "c4" and args.variant == 0
+    t = (load_traffic() if (w.name == "long_16k_causal" and args.variant == 0
                             and not (args.kv_heads or args.bwd or args.split_kv or args.head_dim))
          else None)
     if t is not None:
@@ -278,7 +279,7 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3)
-                        if w.name == "c4" and not (args.kv_heads or args.bwd or args.split_kv or args.head_dim)
+                        if w.name == "long_16k_causal" and not (args.kv_heads or args.bwd or args.split_kv or args.head_dim)
                         else None),
         "dtype": "bf16",
         "data": "synthetic",
@@ -341,7 +342,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="long_16k_causal", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (dQ, dK, dV from dO, O, LSE) instead of the forward")

@@ -59,15 +59,15 @@ class Workload:
 
 
 WORKLOADS: dict[str, Workload] = {
-    "c1": Workload("c1", B=1, H=1, N=256, d=64, causal=False, seed=1,
+    "single_head_256": Workload("single_head_256", B=1, H=1, N=256, d=64, causal=False, seed=1,
                    description="single head: B=1 H=1 N=256 d=64, non-causal"),
-    "c2": Workload("c2", B=8, H=16, N=2048, d=128, causal=False, seed=2,
+    "batch8_2k_d128": Workload("batch8_2k_d128", B=8, H=16, N=2048, d=128, causal=False, seed=2,
                    description="B=8 H=16 N=2048 d=128 (16k tokens, hidden 2048), non-causal"),
-    "c3": Workload("c3", B=8, H=32, N=2048, d=64, causal=True, seed=3,
+    "batch8_2k_d64_causal": Workload("batch8_2k_d64_causal", B=8, H=32, N=2048, d=64, causal=True, seed=3,
                    description="B=8 H=32 N=2048 d=64 (hidden 2048), causal"),
-    "c4": Workload("c4", B=1, H=16, N=16384, d=128, causal=True, seed=4,
+    "long_16k_causal": Workload("long_16k_causal", B=1, H=16, N=16384, d=128, causal=True, seed=4,
                    description="long context: B=1 H=16 N=16384 d=128, causal"),
-    "c5": Workload("c5", B=1, H=16, N=0, d=128, causal=True, seed=5, k_scale=3.0,
+    "varlen16_causal": Workload("varlen16_causal", B=1, H=16, N=0, d=128, causal=True, seed=5, k_scale=3.0,
                    varlen=True, num_seqs=16, min_len=128, max_len=4096,
                    description="packed varlen: 16 sequences, lengths U[128,4096], "
                                "H=16 d=128, causal per sequence, K scaled by 3"),
