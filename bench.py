@@ -322,11 +322,13 @@ def ingest_counters(fetch_csv: str, write_csv: str, steps: int):
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_kernel(path, counter)
         attn = [v for n, vs in vals.items() if "fa2_fwd_kernel" in n for v in vs]
-        copy = [v for n, vs in vals.items() if "fa2_fwd_kernel" not in n and max(vs) > COPY_BYTES / 1024 * 0.5
-                for v in vs]
-        if not attn or not copy:
+        # the calibration copy: the largest other kernel; it moves COPY_BYTES each way, and a
+        # counter that sees it must report at least a quarter of that
+        others = [max(vs) for n, vs in vals.items() if "fa2_fwd_kernel" not in n]
+        copy = max(others) if others else 0.0
+        if not attn or copy < COPY_BYTES / 1024 / 4:
             raise SystemExit(f"{path}: need both the attention kernel and the calibration copy")
-        factor = (COPY_BYTES / 1024) / max(copy)          # counter reads KiB
+        factor = (COPY_BYTES / 1024) / copy               # counter reads KiB
         per_launch = sorted(attn)[len(attn) // 2] * 1024 * factor
         key = "fetch" if counter == "FETCH_SIZE" else "write"
         out[f"{key}_bytes_per_launch"] = per_launch

@@ -1,0 +1,68 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, counter ingestion and the
+algorithmic byte counts the roofline fields use."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from synthetic import WORKLOADS  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_bytes():
+    w = WORKLOADS["long_16k_causal"]
+    # Q, K, V read and O written in bf16, LSE in fp32: 8*B*H*N*d + 4*B*H*N
+    assert bench.algorithmic_bytes(w) == 8 * 16 * 16384 * 128 + 4 * 16 * 16384 == 269484032
+    # grouped-query: K and V have H_kv heads
+    assert bench.algorithmic_bytes(w, kv_heads=4) == 4 * (16 + 4) * 16384 * 128 + 4 * 16 * 16384
+    vl = WORKLOADS["varlen16_causal"]
+    assert bench.algorithmic_bytes(vl, lengths=[10, 20]) == 8 * 16 * 30 * 128 + 4 * 16 * 30
+    # backward: read Q, K, V, O, dO and LSE, write dQ, dK, dV, D written and read once
+    rows = 16 * 16384
+    assert bench.bwd_algorithmic_bytes(w) == 2 * 128 * (4 * rows + 4 * rows) + 12 * rows
+
+
+def _write_counters(path, counter, attn_kib, copy_kib):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for v in attn_kib:
+            wr.writerow({"Kernel_Name": "void fa2_fwd_kernel<128, 64, true, false, 2, 4, 8>(Params)",
+                         "Counter_Name": counter, "Counter_Value": v})
+        wr.writerow({"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": counter, "Counter_Value": copy_kib})
+        wr.writerow({"Kernel_Name": "small_kernel", "Counter_Name": counter, "Counter_Value": 1.0})
+
+
+def test_ingest_counters_scales_by_the_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # The copy moves 1 GiB: FETCH_SIZE reads half of it in KiB (factor 2), WRITE_SIZE all.
+    _write_counters(fetch, "FETCH_SIZE", [100.0, 300.0, 200.0], bench.COPY_BYTES / 1024 / 2)
+    _write_counters(write, "WRITE_SIZE", [50.0, 50.0, 70.0], bench.COPY_BYTES / 1024)
+    bench.ingest_counters(str(fetch), str(write), steps=3)
+    t = json.load(open(tmp_path / "traffic.json"))
+    assert t["kernel_source_sha256"] == bench.kernel_source_hash()
+    assert t["fetch_copy_factor"] == pytest.approx(2.0) and t["write_copy_factor"] == pytest.approx(1.0)
+    assert t["fetch_bytes_per_launch"] == pytest.approx(200.0 * 1024 * 2)     # median x factor
+    assert t["write_bytes_per_launch"] == pytest.approx(50.0 * 1024)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0000")
+    assert bench.load_traffic() is None                                        # stale after a change
+
+
+def test_stored_traffic_matches_the_current_kernel_or_is_ignored():
+    t = bench.load_traffic()
+    if t is not None:
+        assert t["fetch_bytes_per_launch"] > 0 and t["write_bytes_per_launch"] > 0
