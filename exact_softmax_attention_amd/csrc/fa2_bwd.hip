@@ -62,6 +62,7 @@ struct BwdParams {
   float* delta;           // D = rowsum(dO ∘ O), fp32, laid out like lse
   const int* cu_seqlens;  // varlen only
   int nb;                 // batch size, or number of sequences (varlen)
+  int dg;                 // head dimension of the tensors (multiple of 8, <= D; see below)
   int H;                  // query heads
   int Hkv;                // key/value heads
   int g;                  // H / Hkv
@@ -183,8 +184,10 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   if (q0 >= seq_len) return;
   const size_t row0 = q_plane<VARLEN>(p, bi, h) + (size_t)tok0;
   const size_t kvrow0 = kv_plane<VARLEN>(p, bi, h / p.g) + (size_t)tok0;
-  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * D);
-  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * D);
+  const int dg = p.dg;          // row pitch of every tensor, in elements
+  const int growb = 2 * dg;
+  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * dg);
+  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * dg);
   const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
   const int nt = (kv_end + BC - 1) / BC;
 
@@ -198,8 +201,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int kc = 0; kc < TL::NKC; ++kc) {
     u32x4 tq = {0u, 0u, 0u, 0u}, td = tq, to = tq;
-    if (valid) {
-      const size_t off = (row0 + (size_t)qrow) * D + kc * 16 + hl * 8;
+    if (valid && kc * 16 + hl * 8 < dg) {
+      const size_t off = (row0 + (size_t)qrow) * dg + kc * 16 + hl * 8;
       tq = *(const u32x4*)(p.q + off);
       td = *(const u32x4*)(p.dout + off);
       to = *(const u32x4*)(p.o + off);
@@ -224,18 +227,18 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     const int r = o / TL::ROWB;
     const int pch = (o % TL::ROWB) / 16;
     drow_[d] = r;
-    doff[d] = r * TL::ROWB + ((pch ^ dswz<D>(r)) * 16);
+    doff[d] = r * growb + (((pch ^ dswz<D>(r)) % (dg / 8)) * 16);
   }
   auto dma_tile = [&](int j, unsigned char* stage) {
     const int key0 = j * BC;
-    const unsigned char* kt = kh + (size_t)key0 * TL::ROWB;
-    const unsigned char* vt = vh + (size_t)key0 * TL::ROWB;
+    const unsigned char* kt = kh + (size_t)key0 * growb;
+    const unsigned char* vt = vh + (size_t)key0 * growb;
     const uint32_t ks_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
     const uint32_t vs_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
     const int last = seq_len - 1 - key0;   // rows past the end re-read the last valid row
 #pragma unroll
     for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
-      const uint32_t back = (uint32_t)(drow_[d] - min(drow_[d], last)) * TL::ROWB;
+      const uint32_t back = (uint32_t)(drow_[d] - min(drow_[d], last)) * growb;
       dma16(kt, doff[d] - back, ks_a + d * 1024);
       dma16(vt, doff[d] - back, vs_a + d * 1024);
     }
@@ -336,14 +339,14 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   }
 
   if (valid) {
-    uint16_t* out = p.dq + (row0 + (size_t)qrow) * D;
+    uint16_t* out = p.dq + (row0 + (size_t)qrow) * dg;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w = {pack_bf16x2(dqacc[db][4 * g + 0] * p.scale, dqacc[db][4 * g + 1] * p.scale),
                    pack_bf16x2(dqacc[db][4 * g + 2] * p.scale, dqacc[db][4 * g + 3] * p.scale)};
-        *(u32x2*)(out + db * 32 + 8 * g + 4 * hl) = w;
+        if (db * 32 + 8 * g + 4 * hl < dg) *(u32x2*)(out + db * 32 + 8 * g + 4 * hl) = w;
       }
   }
 }
@@ -392,6 +395,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const int k0 = jb * TL::BK;
   if (k0 >= seq_len) return;
   const size_t kvrow0 = kv_plane<VARLEN>(p, bi, hk) + (size_t)tok0;
+  const int dg = p.dg;          // row pitch of every tensor, in elements
+  const int growb = 2 * dg;
 
   // This wave's 32 keys as B fragments of S = Q K^T and dP = dO V^T (key kw0 + l32).
   const int kw0 = k0 + wave * 32;
@@ -401,8 +406,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int kc = 0; kc < TL::NKC; ++kc) {
     u32x4 tk = {0u, 0u, 0u, 0u}, tv = tk;
-    if (kvalid) {
-      const size_t off = (kvrow0 + (size_t)krow) * D + kc * 16 + hl * 8;
+    if (kvalid && kc * 16 + hl * 8 < dg) {
+      const size_t off = (kvrow0 + (size_t)krow) * dg + kc * 16 + hl * 8;
       tk = *(const u32x4*)(p.k + off);
       tv = *(const u32x4*)(p.v + off);
     }
@@ -424,7 +429,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     const int r = o / TL::ROWB;
     const int pch = (o % TL::ROWB) / 16;
     drow_[d] = r;
-    doff[d] = r * TL::ROWB + ((pch ^ dswz<D>(r)) * 16);
+    doff[d] = r * growb + (((pch ^ dswz<D>(r)) % (dg / 8)) * 16);
   }
   auto step_coords = [&](int s, int& q0, size_t& qrow0) {
     const int hq = s / ntq;
@@ -435,14 +440,14 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     int q0;
     size_t qrow0;
     step_coords(s, q0, qrow0);
-    const unsigned char* qt = (const unsigned char*)(p.q + (qrow0 + q0) * D);
-    const unsigned char* dt = (const unsigned char*)(p.dout + (qrow0 + q0) * D);
+    const unsigned char* qt = (const unsigned char*)(p.q + (qrow0 + q0) * dg);
+    const unsigned char* dt = (const unsigned char*)(p.dout + (qrow0 + q0) * dg);
     const uint32_t qs_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
     const uint32_t ds_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
     const int last = seq_len - 1 - q0;    // rows past the end re-read the last valid row
 #pragma unroll
     for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
-      const uint32_t back = (uint32_t)(drow_[d] - min(drow_[d], last)) * TL::ROWB;
+      const uint32_t back = (uint32_t)(drow_[d] - min(drow_[d], last)) * growb;
       dma16(qt, doff[d] - back, qs_a + d * 1024);
       dma16(dt, doff[d] - back, ds_a + d * 1024);
     }
@@ -577,8 +582,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (kvalid) {
-    uint16_t* kout = p.dk + (kvrow0 + (size_t)krow) * D;
-    uint16_t* vout = p.dv + (kvrow0 + (size_t)krow) * D;
+    uint16_t* kout = p.dk + (kvrow0 + (size_t)krow) * dg;
+    uint16_t* vout = p.dv + (kvrow0 + (size_t)krow) * dg;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
@@ -587,8 +592,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
                     pack_bf16x2(dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale)};
         u32x2 wv = {pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]),
                     pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
-        *(u32x2*)(kout + db * 32 + 8 * g + 4 * hl) = wk;
-        *(u32x2*)(vout + db * 32 + 8 * g + 4 * hl) = wv;
+        if (db * 32 + 8 * g + 4 * hl < dg) {
+          *(u32x2*)(kout + db * 32 + 8 * g + 4 * hl) = wk;
+          *(u32x2*)(vout + db * 32 + 8 * g + 4 * hl) = wv;
+        }
       }
   }
 }
@@ -632,6 +639,13 @@ const BwdKernels* bwd_kernels(int d) {
 
 bool aligned_to(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
+// Head dimensions of the backward: multiples of 8 up to 128, run on the D = 64 or 128 kernels
+// with padded columns as in the forward. Q, O, dO, K and V padded columns are either zero in
+// registers (rows loaded by lanes) or duplicates of real columns of the same row (tiles staged
+// to LDS); every product that reaches a written output pairs a padded column with a zero one,
+// and gradient columns past d are never written.
+bool bwd_head_dim(int d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+
 int bwd_launch(const BwdKernels& kk, bool varlen, bool causal, BwdParams p, int nblk_q, int nblk_k,
                long long npairs_q, long long npairs_k, void* stream) {
   int dev = 0;
@@ -656,7 +670,7 @@ int bwd_check(const void* q, const void* k, const void* v, const void* o, const 
               const void* dout, const void* dq, const void* dk, const void* dv, const float* delta,
               int d, float scale) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA2_ERR_NULL_PTR;
-  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (!bwd_head_dim(d)) return FA2_ERR_UNSUPPORTED_HEADDIM;
   const void* b16[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* ptr : b16)
     if (!aligned_to(ptr, 16)) return FA2_ERR_MISALIGNED;
@@ -691,7 +705,7 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
             const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int H_kv,
             int N, int d, int causal, float scale, void* stream) {
   if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N < 0) return FA2_ERR_BAD_SHAPE;
-  if (N == 0) return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (N == 0) return bwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
   if (st != FA2_OK) return st;
   const long long nblk = ((long long)N + 127) / 128;
@@ -701,12 +715,13 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   bwd_fill(p, q, k, v, o, lse, dout, dq, dk, dv, delta, scale);
   p.cu_seqlens = nullptr;
   p.nb = B;
+  p.dg = d;
   p.H = H;
   p.Hkv = H_kv;
   p.g = H / H_kv;
   p.N = N;
   p.T = N;
-  const BwdKernels& kk = *bwd_kernels(d);
+  const BwdKernels& kk = *bwd_kernels(d <= 64 ? 64 : 128);
   const long long nblk_q = ((long long)N + kk.dq_br - 1) / kk.dq_br;
   return bwd_launch(kk, false, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
 }
@@ -718,7 +733,7 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   if (H <= 0 || H_kv <= 0 || H % H_kv != 0 || num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
     return FA2_ERR_BAD_SHAPE;
   if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
-    return (d == 64 || d == 128) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+    return bwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   if (!cu_seqlens) return FA2_ERR_NULL_PTR;
   if (!aligned_to(cu_seqlens, 4)) return FA2_ERR_MISALIGNED;
   int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
@@ -730,12 +745,13 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   bwd_fill(p, q, k, v, o, lse, dout, dq, dk, dv, delta, scale);
   p.cu_seqlens = cu_seqlens;
   p.nb = num_seqs;
+  p.dg = d;
   p.H = H;
   p.Hkv = H_kv;
   p.g = H / H_kv;
   p.N = max_seqlen;
   p.T = total_tokens;
-  const BwdKernels& kk = *bwd_kernels(d);
+  const BwdKernels& kk = *bwd_kernels(d <= 64 ? 64 : 128);
   const long long nblk_q = ((long long)max_seqlen + kk.dq_br - 1) / kk.dq_br;
   return bwd_launch(kk, true, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
 }

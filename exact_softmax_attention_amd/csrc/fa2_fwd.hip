@@ -1004,7 +1004,7 @@ const char* fa2_status_str(int status) {
     case FA2_ERR_NULL_PTR: return "a required pointer is NULL";
     case FA2_ERR_BAD_SHAPE: return "bad shape (B, H must be > 0, N >= 0; varlen sizes consistent)";
     case FA2_ERR_UNSUPPORTED_HEADDIM:
-      return "unsupported head dimension (forward: multiple of 8 up to 256; backward: 64 or 128)";
+      return "unsupported head dimension (a multiple of 8 up to 256 forward, up to 128 backward)";
     case FA2_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 B, lse 4 B)";
     case FA2_ERR_BAD_SCALE: return "scale is not finite";
     case FA2_ERR_NO_DEVICE: return "no usable HIP device";

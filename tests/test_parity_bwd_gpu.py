@@ -112,6 +112,17 @@ def test_bwd_varlen(d):
         _check_grad(_f64(dv), rv, tag + " dV")
 
 
+@pytest.mark.parametrize("d", [8, 32, 80, 96])
+def test_bwd_padded_head_dims(d):
+    """Head dims that are multiples of 8 below 128 run on the 64/128 kernels with padding."""
+    for N, H_kv in ((100, 4), (257, 2)):
+        q, k, v = make_qkv(2, 4, N, d, seed=260 + N + d, H_kv=H_kv)
+        do = _dout(q.shape, 360 + N + d)
+        for causal in (False, True):
+            print(f"[case] bwd padded d={d} N={N} H_kv={H_kv} causal={causal}", flush=True)
+            _compare(q, k, v, do, causal, 1.0 / np.sqrt(d), f"bwd d{d} N{N} 4/{H_kv} causal={causal}")
+
+
 def test_bwd_scale_edges():
     q, k, v = make_qkv(1, 2, 200, 64, seed=230)
     do = _dout(q.shape, 330)
