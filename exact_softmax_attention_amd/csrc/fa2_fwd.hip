@@ -154,10 +154,12 @@ constexpr float kLazyTau = 8.0f;
 constexpr float kOptLimit = 256.0f;   // 2^kLazyTau
 
 // LA: how many operand fragments are read from LDS ahead of the MFMA that consumes them
-// (0 leaves the order to the compiler's scheduler).
-template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW = 4>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
-                          amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+// (0 leaves the order to the compiler's scheduler). OCC: waves per SIMD the kernel is built
+// for (its registers are limited to 512 / OCC per lane); more resident waves let one wave's
+// softmax run while another's MFMAs occupy the matrix core.
+template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW = 4,
+          int OCC = (D == 256 ? 1 : 2)>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_fwd_kernel(Params p) {
   using TL = Tile<D, BC, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
@@ -808,7 +810,7 @@ struct Variant {
   KernelFn varlen[2];  // [causal]
 };
 
-template <int D, int BC, int MODE, int LA = 0, int NW = 4>
+template <int D, int BC, int MODE, int LA = 0, int NW = 4, int OCC = (D == 256 ? 1 : 2)>
 Variant make_variant(const char* name) {
   using TL = Tile<D, BC, NW>;
   Variant v;
@@ -818,10 +820,10 @@ Variant make_variant(const char* name) {
   v.br = TL::BR;
   v.bc = BC;
   v.lds = TL::LDS_BYTES;
-  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false, MODE, LA, NW>;
-  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false, MODE, LA, NW>;
-  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true, MODE, LA, NW>;
-  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true, MODE, LA, NW>;
+  v.fixed[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, false, MODE, LA, NW, OCC>;
+  v.fixed[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, false, MODE, LA, NW, OCC>;
+  v.varlen[0] = (KernelFn)&fa2_fwd_kernel<D, BC, false, true, MODE, LA, NW, OCC>;
+  v.varlen[1] = (KernelFn)&fa2_fwd_kernel<D, BC, true, true, MODE, LA, NW, OCC>;
   return v;
 }
 
@@ -844,20 +846,27 @@ Variant make_variant_pp(const char* name) {
 
 // Variant 0 of each head dimension is the default; the others exist for tuning and tests.
 const Variant* variants_for(int d, int* count) {
+  // d = 64: the O~ accumulator is half that of d = 128, so a 64-key tile fits in 128
+  // registers and four waves share each SIMD (two 8-wave workgroups per CU, 32 KB of LDS
+  // each); the softmax work, which per flop is twice that of d = 128, then overlaps the
+  // matrix work of the other waves.
   static const Variant v64[] = {
+      make_variant<64, 64, kOptimistic, 4, 8, 4>("d64_w8_bc64_occ4_la4"),
       make_variant<64, 128, kOptimistic, 4>("d64_bc128_opt_la4"),
       make_variant<64, 128, kOptimistic>("d64_bc128_opt"),
       make_variant<64, 128, kLazy, 4>("d64_bc128_lazy_la4"),
       make_variant<64, 128, kExact>("d64_bc128_exact"),
       make_variant_pp<64, 64, 4>("d64_pp_bc64_la4"),
-      make_variant<64, 128, kOptimistic, 4, 8>("d64_w8_bc128_opt_la4")};
+      make_variant<64, 128, kOptimistic, 4, 8>("d64_w8_bc128_opt_la4"),
+      make_variant<64, 64, kOptimistic, 4, 4, 3>("d64_bc64_occ3_la4")};
   static const Variant v128[] = {
       make_variant<128, 64, kOptimistic, 4, 8>("d128_w8_bc64_opt_la4"),
       make_variant<128, 64, kOptimistic, 4>("d128_bc64_opt_la4"),
       make_variant<128, 64, kOptimistic>("d128_bc64_opt"),
       make_variant<128, 64, kLazy, 4>("d128_bc64_lazy_la4"),
       make_variant<128, 64, kExact>("d128_bc64_exact"),
-      make_variant_pp<128, 64, 4>("d128_pp_bc64_la4")};
+      make_variant_pp<128, 64, 4>("d128_pp_bc64_la4"),
+      make_variant<128, 32, kOptimistic, 4, 4, 3>("d128_bc32_occ3_la4")};
   // d = 256: one wave per SIMD (the O~ accumulator alone is 128 registers), so the
   // ping-pong family, which needs two waves per SIMD, has no d = 256 member.
   static const Variant v256[] = {
