@@ -41,6 +41,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "exact_softmax_attention_amd", "csrc", name) f
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_long16k_traffic.json")
 WORKLOAD_NAMES = ("single_head_256", "batch8_2k_d128", "batch8_2k_d64_causal", "long_16k_causal", "varlen16_causal")
 COPY_BYTES = 1 << 30   # the calibration copy kernel moves 1 GiB in and 1 GiB out
+WARMUP_SECONDS = 0.5   # default warmup: untimed work before the timed steps, in seconds
 
 
 def kernel_source_hash() -> str:
@@ -209,8 +210,23 @@ def run(args):
         del src, dst
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
+    if args.warmup is None:
+        # Untimed steps until about WARMUP_SECONDS of work has run, so that the shader clock
+        # has settled (a short kernel timed from a cold start reads up to 20% slow). The
+        # probe steps count towards the reported warmup.
         step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        per_step = (time.perf_counter() - t0) / 4
+        args.warmup = 5 + max(5, min(20000, math.ceil(WARMUP_SECONDS / max(per_step, 1e-6))))
+        for _ in range(args.warmup - 5):
+            step()
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -343,7 +359,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed warmup steps (default: as many as take about {WARMUP_SECONDS} s, at least 10)")
     ap.add_argument("--workload", default="long_16k_causal", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--bwd", action="store_true",
