@@ -277,19 +277,25 @@ void fa2_fwd_kernel(Params p) {
     }
   };
 
-  // Per-lane LDS read offsets (bytes inside a stage), precomputed once.
+  // Per-lane LDS read offsets (bytes inside a stage), precomputed once. The swizzles only
+  // permute the low four bits of a row's 16-byte chunk index, so logical chunk c + 16 lies
+  // exactly 256 bytes after chunk c: offsets are kept for the first 16 chunks of a row and
+  // the rest reached through the instructions' immediate offset (at d = 256 this keeps 12
+  // registers fewer; at d <= 128 every offset is within the first 16 chunks anyway).
   //  K (A operand of S^T): row kb*32 + l32, logical chunk 2*kc + hl.
-  int kaddr[TL::NKC];
+  constexpr int NKA = TL::NKC < 8 ? TL::NKC : 8;
+  int kaddr[NKA];
 #pragma unroll
-  for (int kc = 0; kc < TL::NKC; ++kc)
+  for (int kc = 0; kc < NKA; ++kc)
     kaddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ TL::kswz(l32)) * 16);
   //  V^T (A operand of O^T) by two transposed 8-byte reads per fragment from row-major V:
   //  the lane supplies row 16c + 8t + 4hl + (lane%16)/4 and columns 32db + 16((lane/16)%2) +
   //  4(lane%4) .. +3, and receives keys 16c + 8t + 4hl + 0..3 of column d = 32db + l32.
   const int vr = 4 * hl + ((lane & 15) >> 2);
-  int vaddr[TL::NDB];
+  constexpr int NVA = TL::NDB < 4 ? TL::NDB : 4;
+  int vaddr[NVA];
 #pragma unroll
-  for (int db = 0; db < TL::NDB; ++db) {
+  for (int db = 0; db < NVA; ++db) {
     const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     vaddr[db] = TL::TILEB + vr * TL::ROWB + (((col >> 3) ^ TL::vswz(vr)) * 16) + (col & 7) * 2;
   }
@@ -315,7 +321,7 @@ void fa2_fwd_kernel(Params p) {
       s[kb] = (f32x16){};
 #pragma unroll
       for (int kc = 0; kc < TL::NKC; ++kc) {
-        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + kaddr[kc]);
+        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + (kc >> 3) * 256 + kaddr[kc & 7]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
       }
     }
@@ -419,7 +425,7 @@ void fa2_fwd_kernel(Params p) {
       const bf16x8 pf = as_bf16x8(pw[c]);
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db) {
-        const unsigned char* va = stage + vaddr[db] + 16 * c * TL::ROWB;
+        const unsigned char* va = stage + vaddr[db & 3] + (db >> 2) * 256 + 16 * c * TL::ROWB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va + 8 * TL::ROWB));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -867,12 +873,17 @@ const Variant* variants_for(int d, int* count) {
       make_variant<128, 64, kExact>("d128_bc64_exact"),
       make_variant_pp<128, 64, 4>("d128_pp_bc64_la4"),
       make_variant<128, 32, kOptimistic, 4, 4, 3>("d128_bc32_occ3_la4")};
-  // d = 256: one wave per SIMD (the O~ accumulator alone is 128 registers), so the
-  // ping-pong family, which needs two waves per SIMD, has no d = 256 member.
+  // d = 256: the O~ accumulator alone is 128 registers. With 32-key tiles (and the K/V read
+  // offsets past the 16th chunk of a row folded into immediates) a wave fits in 256
+  // registers, so two waves share each SIMD in an 8-wave workgroup; the 64-key forms run one
+  // wave per SIMD. The ping-pong family, which needs two waves per SIMD at 64-key tiles, has
+  // no d = 256 member.
   static const Variant v256[] = {
+      make_variant<256, 32, kOptimistic, 4, 8, 2>("d256_w8_bc32_occ2_la4"),
       make_variant<256, 64, kOptimistic, 4>("d256_bc64_opt_la4"),
       make_variant<256, 32, kOptimistic, 4>("d256_bc32_opt_la4"),
-      make_variant<256, 64, kExact>("d256_bc64_exact")};
+      make_variant<256, 64, kExact>("d256_bc64_exact"),
+      make_variant<256, 32, kOptimistic, 4, 4, 2>("d256_bc32_occ2_la4")};
   if (d == 64) {
     *count = (int)(sizeof(v64) / sizeof(v64[0]));
     return v64;
