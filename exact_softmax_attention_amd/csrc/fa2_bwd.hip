@@ -161,8 +161,8 @@ struct DqTile {
   static_assert(BC % 32 == 0 && DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
 };
 
-template <int D, int BC, bool CAUSAL, bool VARLEN, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+template <int D, int BC, bool CAUSAL, bool VARLEN, int NW, int OCC>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_bwd_dq_kernel(BwdParams p) {
   using TL = DqTile<D, BC, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
@@ -360,7 +360,7 @@ struct DkvTile {
   static constexpr int BK = 32 * WAVES;             // keys per workgroup
   static constexpr int ROWB = 2 * D;
   static constexpr int TILEB = BQ * ROWB;           // one Q (or dO) tile
-  static constexpr int VECB = 256;                  // one L (or D) vector, BQ fp32
+  static constexpr int VECB = 256;                  // one L (or D) vector: 64 fp32 loaded, first BQ used
   static constexpr int STAGEB = 2 * TILEB + 2 * VECB;
   static constexpr int LDS_BYTES = 2 * STAGEB;
   static constexpr int DMA_PER_WAVE = TILEB / 1024 / WAVES;
@@ -369,16 +369,19 @@ struct DkvTile {
   static constexpr int NDB = D / 32;
   static constexpr int NPC = BQ / 16;
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(BQ == 64, "one 256-byte direct load per statistics vector");
+  static_assert(BQ == 64 || BQ == 32, "statistics vectors are one 256-byte direct load");
   static_assert(DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
 };
 
-template <int D, int BQ, bool CAUSAL, bool VARLEN, int OCC>
+// KLDS: the wave's K rows are kept in LDS (stored once, in the swizzled layout of the Q row
+// reads) instead of 32 registers, which lets d = 128 run two waves per SIMD.
+template <int D, int BQ, bool CAUSAL, bool VARLEN, int OCC, bool KLDS>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_bwd_dkdv_kernel(BwdParams p) {
   using TL = DkvTile<D, BQ>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[KLDS ? TL::BK * TL::ROWB : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -464,6 +467,15 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int kc = 0; kc < TL::NKC; ++kc)
     raddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ dswz<D>(l32)) * 16);
+  // K rows of this wave in LDS: row l32 of the wave's 32-row slab, chunk 2kc + hl, at the
+  // same swizzled offsets as the Q row reads (the slab starts at a multiple of 32 rows, and
+  // the swizzle depends on the row's low four bits only). Published by the barrier that
+  // precedes the first step.
+  const uint32_t kslab = (uint32_t)wave * 32u * TL::ROWB;
+  if constexpr (KLDS) {
+#pragma unroll
+    for (int kc = 0; kc < TL::NKC; ++kc) *(bf16x8*)(kst + kslab + raddr[kc]) = kf[kc];
+  }
   // Transposed reads (A operands dO^T and Q^T), as K^T in the dQ kernel.
   const int tr0 = 4 * hl + ((lane & 15) >> 2);
   int taddr_lo[TL::NDB], taddr_hi[TL::NDB];
@@ -496,7 +508,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
       for (int kc = 0; kc < TL::NKC; ++kc) {
         const bf16x8 qa = *(const bf16x8*)(stage + qb * 32 * TL::ROWB + raddr[kc]);
         const bf16x8 da = *(const bf16x8*)(stage + TL::TILEB + qb * 32 * TL::ROWB + raddr[kc]);
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kc], s[qb], 0, 0, 0);
+        const bf16x8 kk = KLDS ? *(const bf16x8*)(kst + kslab + raddr[kc]) : kf[kc];
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kk, s[qb], 0, 0, 0);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kc], dp[qb], 0, 0, 0);
       }
     }
@@ -613,27 +626,30 @@ struct BwdKernels {
   KernelFn dkdv[2][2];
 };
 
-template <int D, int BC_DQ, int NW_DQ, int OCC_DKDV>
+template <int D, int BC_DQ, int NW_DQ, int OCC_DQ, int OCC_DKDV, int BQ_DKDV, bool KLDS>
 BwdKernels make_bwd() {
   BwdKernels k;
   k.dq_bc = BC_DQ;
   k.dq_br = DqTile<D, BC_DQ, NW_DQ>::BR;
   k.dq_threads = DqTile<D, BC_DQ, NW_DQ>::THREADS;
-  k.dkdv_threads = DkvTile<D, 64>::THREADS;
-  k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false, NW_DQ>;
-  k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false, NW_DQ>;
-  k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true, NW_DQ>;
-  k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true, NW_DQ>;
-  k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, false, false, OCC_DKDV>;
-  k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, true, false, OCC_DKDV>;
-  k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, false, true, OCC_DKDV>;
-  k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, 64, true, true, OCC_DKDV>;
+  k.dkdv_threads = DkvTile<D, BQ_DKDV>::THREADS;
+  k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false, NW_DQ, OCC_DQ>;
+  k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false, NW_DQ, OCC_DQ>;
+  k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true, NW_DQ, OCC_DQ>;
+  k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true, NW_DQ, OCC_DQ>;
+  k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, false, OCC_DKDV, KLDS>;
+  k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, false, OCC_DKDV, KLDS>;
+  k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, true, OCC_DKDV, KLDS>;
+  k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, true, OCC_DKDV, KLDS>;
   return k;
 }
 
 const BwdKernels* bwd_kernels(int d) {
-  static const BwdKernels k64 = make_bwd<64, 64, 4, 2>();
-  static const BwdKernels k128 = make_bwd<128, 32, 4, 1>();
+  // <D, dQ key tile, dQ waves, dQ waves per SIMD, dK/dV waves per SIMD, dK/dV query step,
+  //  K rows of dK/dV in LDS>: chosen so each kernel keeps as many waves per SIMD as its
+  //  registers allow (d = 128 dK/dV: 32-query steps and K in LDS bring it from one to two).
+  static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 3, 32, true>();
+  static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 2, 32, true>();
   return d == 64 ? &k64 : d == 128 ? &k128 : nullptr;
 }
 
