@@ -79,9 +79,13 @@ struct BwdParams {
 // access patterns used on one tile are free of bank conflicts: 16-byte row reads by 16
 // consecutive rows at one logical chunk, and transposed 8-byte reads of 4 consecutive rows
 // (starting at a multiple of 4) by 4 consecutive chunks. Period 16 in the row index.
+// D = 256 rows (512 bytes, two bank sweeps) use the D = 128 pattern on the low four bits of
+// the chunk index. Every swizzle value is below 16, so logical chunk c + 16 of a row lies 256
+// bytes after chunk c: read offsets are kept for chunks 0..15 and the rest reached through
+// the instructions' immediate offset (roff/toff below).
 template <int D>
 __device__ __forceinline__ int dswz(int row) {
-  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+  return D >= 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
                   : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
@@ -157,7 +161,7 @@ struct DqTile {
   static constexpr int NKC = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int NPC = BC / 16;
-  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
   static_assert(BC % 32 == 0 && DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
 };
 
@@ -245,20 +249,25 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   };
 
   // Row reads (A operands of S^T and dP^T): row kb*32 + l32, logical chunk 2kc + hl.
-  int raddr[TL::NKC];
+  constexpr int NRA = TL::NKC < 8 ? TL::NKC : 8;
+  int raddr[NRA];
 #pragma unroll
-  for (int kc = 0; kc < TL::NKC; ++kc)
+  for (int kc = 0; kc < NRA; ++kc)
     raddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ dswz<D>(l32)) * 16);
+  auto roff = [&](int kc) { return raddr[kc & 7] + (kc >> 3) * 256; };
   // Transposed reads of K (A operand K^T of dQ^T): rows 16c + 4hl + (lane%16)/4 (low half of
   // the fragment) and the same + 8 (high half), columns 32db + 16((lane/16)%2) + 4(lane%4).
   const int tr0 = 4 * hl + ((lane & 15) >> 2);
-  int taddr_lo[TL::NDB], taddr_hi[TL::NDB];
+  constexpr int NTA = TL::NDB < 4 ? TL::NDB : 4;
+  int taddr_lo[NTA], taddr_hi[NTA];
 #pragma unroll
-  for (int db = 0; db < TL::NDB; ++db) {
+  for (int db = 0; db < NTA; ++db) {
     const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     taddr_lo[db] = tr0 * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0)) * 16) + (col & 7) * 2;
     taddr_hi[db] = (tr0 + 8) * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0 + 8)) * 16) + (col & 7) * 2;
   }
+  auto toff_lo = [&](int db) { return taddr_lo[db & 3] + (db >> 2) * 256; };
+  auto toff_hi = [&](int db) { return taddr_hi[db & 3] + (db >> 2) * 256; };
 
   f32x16 dqacc[TL::NDB];
 #pragma unroll
@@ -274,8 +283,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
       dp[kb] = (f32x16){};
 #pragma unroll
       for (int kc = 0; kc < TL::NKC; ++kc) {
-        const bf16x8 ka = *(const bf16x8*)(stage + kb * 32 * TL::ROWB + raddr[kc]);
-        const bf16x8 va = *(const bf16x8*)(stage + TL::TILEB + kb * 32 * TL::ROWB + raddr[kc]);
+        const bf16x8 ka = *(const bf16x8*)(stage + kb * 32 * TL::ROWB + roff(kc));
+        const bf16x8 va = *(const bf16x8*)(stage + TL::TILEB + kb * 32 * TL::ROWB + roff(kc));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kc], dp[kb], 0, 0, 0);
       }
@@ -316,8 +325,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db) {
         const unsigned char* base = stage + 16 * c * TL::ROWB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + taddr_lo[db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + taddr_hi[db]));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + toff_lo(db)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + toff_hi(db)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf, dqacc[db], 0, 0, 0);
       }
@@ -368,7 +377,7 @@ struct DkvTile {
   static constexpr int NKC = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int NPC = BQ / 16;
-  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
   static_assert(BQ == 64 || BQ == 32, "statistics vectors are one 256-byte direct load");
   static_assert(DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
 };
@@ -463,10 +472,12 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   };
 
   // Row reads (A operands of S and dP): row qb*32 + l32, logical chunk 2kc + hl.
-  int raddr[TL::NKC];
+  constexpr int NRA = TL::NKC < 8 ? TL::NKC : 8;
+  int raddr[NRA];
 #pragma unroll
-  for (int kc = 0; kc < TL::NKC; ++kc)
+  for (int kc = 0; kc < NRA; ++kc)
     raddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ dswz<D>(l32)) * 16);
+  auto roff = [&](int kc) { return raddr[kc & 7] + (kc >> 3) * 256; };
   // K rows of this wave in LDS: row l32 of the wave's 32-row slab, chunk 2kc + hl, at the
   // same swizzled offsets as the Q row reads (the slab starts at a multiple of 32 rows, and
   // the swizzle depends on the row's low four bits only). Published by the barrier that
@@ -474,17 +485,20 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const uint32_t kslab = (uint32_t)wave * 32u * TL::ROWB;
   if constexpr (KLDS) {
 #pragma unroll
-    for (int kc = 0; kc < TL::NKC; ++kc) *(bf16x8*)(kst + kslab + raddr[kc]) = kf[kc];
+    for (int kc = 0; kc < TL::NKC; ++kc) *(bf16x8*)(kst + kslab + roff(kc)) = kf[kc];
   }
   // Transposed reads (A operands dO^T and Q^T), as K^T in the dQ kernel.
   const int tr0 = 4 * hl + ((lane & 15) >> 2);
-  int taddr_lo[TL::NDB], taddr_hi[TL::NDB];
+  constexpr int NTA = TL::NDB < 4 ? TL::NDB : 4;
+  int taddr_lo[NTA], taddr_hi[NTA];
 #pragma unroll
-  for (int db = 0; db < TL::NDB; ++db) {
+  for (int db = 0; db < NTA; ++db) {
     const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     taddr_lo[db] = tr0 * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0)) * 16) + (col & 7) * 2;
     taddr_hi[db] = (tr0 + 8) * TL::ROWB + (((col >> 3) ^ dswz<D>(tr0 + 8)) * 16) + (col & 7) * 2;
   }
+  auto toff_lo = [&](int db) { return taddr_lo[db & 3] + (db >> 2) * 256; };
+  auto toff_hi = [&](int db) { return taddr_hi[db & 3] + (db >> 2) * 256; };
 
   f32x16 dkacc[TL::NDB], dvacc[TL::NDB];
 #pragma unroll
@@ -506,9 +520,9 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
       dp[qb] = (f32x16){};
 #pragma unroll
       for (int kc = 0; kc < TL::NKC; ++kc) {
-        const bf16x8 qa = *(const bf16x8*)(stage + qb * 32 * TL::ROWB + raddr[kc]);
-        const bf16x8 da = *(const bf16x8*)(stage + TL::TILEB + qb * 32 * TL::ROWB + raddr[kc]);
-        const bf16x8 kk = KLDS ? *(const bf16x8*)(kst + kslab + raddr[kc]) : kf[kc];
+        const bf16x8 qa = *(const bf16x8*)(stage + qb * 32 * TL::ROWB + roff(kc));
+        const bf16x8 da = *(const bf16x8*)(stage + TL::TILEB + qb * 32 * TL::ROWB + roff(kc));
+        const bf16x8 kk = KLDS ? *(const bf16x8*)(kst + kslab + roff(kc)) : kf[kc];
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kk, s[qb], 0, 0, 0);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kc], dp[qb], 0, 0, 0);
       }
@@ -568,10 +582,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
       for (int db = 0; db < TL::NDB; ++db) {
         const unsigned char* qbase = stage + 16 * c * TL::ROWB;
         const unsigned char* dbase = stage + TL::TILEB + 16 * c * TL::ROWB;
-        const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + taddr_lo[db]));
-        const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + taddr_hi[db]));
-        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + taddr_lo[db]));
-        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + taddr_hi[db]));
+        const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + toff_lo(db)));
+        const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + toff_hi(db)));
+        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + toff_lo(db)));
+        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + toff_hi(db)));
         const bf16x8 da = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
         const bf16x8 qa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
         dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, pf, dvacc[db], 0, 0, 0);
@@ -650,17 +664,21 @@ const BwdKernels* bwd_kernels(int d) {
   //  registers allow (d = 128 dK/dV: 32-query steps and K in LDS bring it from one to two).
   static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 3, 32, true>();
   static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 2, 32, true>();
-  return d == 64 ? &k64 : d == 128 ? &k128 : nullptr;
+  // d = 256: the dQ^T, dK^T and dV^T accumulators are 128 registers each, so both kernels run
+  // one wave per SIMD (dK/dV: 129 KB of LDS, one workgroup per CU).
+  static const BwdKernels k256 = make_bwd<256, 32, 4, 1, 1, 32, true>();
+  return d == 64 ? &k64 : d == 128 ? &k128 : d == 256 ? &k256 : nullptr;
 }
 
 bool aligned_to(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
-// Head dimensions of the backward: multiples of 8 up to 128, run on the D = 64 or 128 kernels
-// with padded columns as in the forward. Q, O, dO, K and V padded columns are either zero in
+// Head dimensions of the backward: multiples of 8 up to 256, run on the D = 64, 128 or 256
+// kernels with padded columns as in the forward. Q, O, dO, K and V padded columns are either zero in
 // registers (rows loaded by lanes) or duplicates of real columns of the same row (tiles staged
 // to LDS); every product that reaches a written output pairs a padded column with a zero one,
 // and gradient columns past d are never written.
-bool bwd_head_dim(int d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+bool bwd_head_dim(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
+int bwd_padded_dim(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
 
 int bwd_launch(const BwdKernels& kk, bool varlen, bool causal, BwdParams p, int nblk_q, int nblk_k,
                long long npairs_q, long long npairs_k, void* stream) {
@@ -737,7 +755,7 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.g = H / H_kv;
   p.N = N;
   p.T = N;
-  const BwdKernels& kk = *bwd_kernels(d <= 64 ? 64 : 128);
+  const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
   const long long nblk_q = ((long long)N + kk.dq_br - 1) / kk.dq_br;
   return bwd_launch(kk, false, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
 }
@@ -767,7 +785,7 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   p.g = H / H_kv;
   p.N = max_seqlen;
   p.T = total_tokens;
-  const BwdKernels& kk = *bwd_kernels(d <= 64 ? 64 : 128);
+  const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
   const long long nblk_q = ((long long)max_seqlen + kk.dq_br - 1) / kk.dq_br;
   return bwd_launch(kk, true, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
 }

@@ -46,8 +46,7 @@ enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_NULL_PTR = 1,            /* a required pointer is NULL */
   FA2_ERR_BAD_SHAPE = 2,           /* B, H or H_kv <= 0, H_kv not dividing H, N < 0, ... */
-  FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* forward, merge: d not a multiple of 8 in [8, 256];
-                                      backward: d not a multiple of 8 in [8, 128] */
+  FA2_ERR_UNSUPPORTED_HEADDIM = 3, /* d not a multiple of 8 in [8, 256] */
   FA2_ERR_MISALIGNED = 4,          /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
   FA2_ERR_BAD_SCALE = 5,           /* scale is NaN or infinite */
   FA2_ERR_NO_DEVICE = 6,           /* no usable HIP device is current */
@@ -190,9 +189,9 @@ int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, lo
  *   lse            : fp32 [B, H, N], the forward's logsumexp (natural log);
  *   delta          : fp32 [B, H, N] caller-provided buffer, overwritten with D (it is the
  *                    only intermediate; the library allocates nothing).
- *   H_kv must divide H. d is a multiple of 8 up to 128 (64 and 128 natively, others padded
- *   as in the forward; d > 128 has no backward); causal and scale as for the forward (same
- *   scale as the forward).
+ *   H_kv must divide H. d is a multiple of 8 up to 256 (64, 128 and 256 natively, others
+ *   padded as in the forward); causal and scale as for the forward (same scale as the
+ *   forward).
  *   dq, dk, dv and delta are fully overwritten on success; they must not alias the inputs.
  * Two kernels run in order on stream (dQ and D, then dK and dV); no atomics are used, so the
  * gradients are bitwise reproducible. Validation, ownership and zero-size rules as fa2_fwd.

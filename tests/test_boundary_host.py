@@ -190,7 +190,7 @@ def _bwd_varlen(cu=FAKE, S=2, maxlen=16, T=32, H=4, H_kv=4, d=64, causal=0, scal
     (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1),
     (dict(dk=None), 1), (dict(dv=None), 1), (dict(delta=None), 1),
     (dict(B=0), 2), (dict(H_kv=3), 2), (dict(H_kv=0), 2), (dict(N=-1), 2),
-    (dict(d=100), 3), (dict(d=136), 3), (dict(d=256), 3), (dict(dq=FAKE + 8), 4), (dict(delta=FAKE + 2), 4), (dict(o=FAKE + 4), 4),
+    (dict(d=100), 3), (dict(d=264), 3), (dict(d=4), 3), (dict(dq=FAKE + 8), 4), (dict(delta=FAKE + 2), 4), (dict(o=FAKE + 4), 4),
     (dict(scale=float("nan")), 5), (dict(N=1 << 30, H=64, H_kv=64), 9),
 ])
 def test_bwd_validation(kwargs, code):

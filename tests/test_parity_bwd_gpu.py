@@ -71,7 +71,7 @@ def _compare(q, k, v, do, causal, scale, tag):
     _check_grad(_f64(dv), rv, tag + " dV")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 17, 100, 128, 129, 257])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small(d, N, causal):
@@ -81,7 +81,7 @@ def test_bwd_small(d, N, causal):
     _compare(q, k, v, do, causal, 1.0 / np.sqrt(d), f"bwd d{d} N{N} causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("H_kv", [1, 2])
 def test_bwd_gqa(d, H_kv):
     q, k, v = make_qkv(2, 4, 300, d, seed=210 + H_kv + d, H_kv=H_kv)
@@ -91,7 +91,7 @@ def test_bwd_gqa(d, H_kv):
         _compare(q, k, v, do, causal, 1.0 / np.sqrt(d), f"bwd gqa d{d} 4/{H_kv} causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_bwd_varlen(d):
     lengths = [1, 127, 0, 128, 129, 300, 64, 2]
     H, H_kv = 4, 2
@@ -112,9 +112,9 @@ def test_bwd_varlen(d):
         _check_grad(_f64(dv), rv, tag + " dV")
 
 
-@pytest.mark.parametrize("d", [8, 32, 80, 96])
+@pytest.mark.parametrize("d", [8, 32, 80, 96, 136, 200, 248])
 def test_bwd_padded_head_dims(d):
-    """Head dims that are multiples of 8 below 128 run on the 64/128 kernels with padding."""
+    """Head dims that are multiples of 8 below 256 run on the 64/128/256 kernels with padding."""
     for N, H_kv in ((100, 4), (257, 2)):
         q, k, v = make_qkv(2, 4, N, d, seed=260 + N + d, H_kv=H_kv)
         do = _dout(q.shape, 360 + N + d)
@@ -148,6 +148,23 @@ def test_bwd_long_full_heads():
         _check_grad(_f64(dk[0, h]), rk, f"bwd long h{h} dK")
         _check_grad(_f64(dv[0, h]), rv, f"bwd long h{h} dV")
         del rq, rk, rv
+
+
+def test_bwd_d256_long_full_head():
+    """d = 256 (one wave per SIMD in both kernels) over 4096 causal rows, four heads in one
+    launch; head 2 compared in full against the oracle."""
+    B, H, N, d = 1, 4, 4096, 256
+    q, k, v = make_qkv(B, H, N, d, seed=270)
+    do = _dout(q.shape, 370)
+    scale = 1.0 / np.sqrt(d)
+    print("[case] bwd B1 H4 N4096 d256 causal", flush=True)
+    dq, dk, dv = _run(q, k, v, do, True, scale)
+    h = 2
+    rq, rk, rv = attention_backward_head(q[0, h].double().numpy(), k[0, h].double().numpy(),
+                                         v[0, h].double().numpy(), do[0, h].double().numpy(), True, scale)
+    _check_grad(_f64(dq[0, h]), rq, "bwd d256 long dQ")
+    _check_grad(_f64(dk[0, h]), rk, "bwd d256 long dK")
+    _check_grad(_f64(dv[0, h]), rv, "bwd d256 long dV")
 
 
 def test_bwd_deterministic():
