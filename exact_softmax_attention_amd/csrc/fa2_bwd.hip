@@ -686,14 +686,16 @@ int bwd_launch(const BwdKernels& kk, bool varlen, bool causal, BwdParams p, int 
   if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
   const int v = varlen ? 1 : 0, c = causal ? 1 : 0;
   p.nblk = nblk_q;
-  p.heads_per_xcd = (npairs_q % 8 == 0) ? (int)(npairs_q / 8) : 0;
+  // Per-XCD pair ranges for fixed-length batches; varlen uses the plain heaviest-first order
+  // (with unequal sequence lengths the per-XCD ranges get unequal shares, as in the forward).
+  p.heads_per_xcd = (!varlen && npairs_q % 8 == 0) ? (int)(npairs_q / 8) : 0;
   void* args[] = {&p};
   hipError_t e = hipLaunchKernel(kk.dq[v][c], dim3((unsigned)(nblk_q * npairs_q)),
                                  dim3((unsigned)kk.dq_threads), args, 0, (hipStream_t)stream);
   if (e != hipSuccess) return FA2_ERR_LAUNCH;
   BwdParams p2 = p;
   p2.nblk = nblk_k;
-  p2.heads_per_xcd = (npairs_k % 8 == 0) ? (int)(npairs_k / 8) : 0;
+  p2.heads_per_xcd = (!varlen && npairs_k % 8 == 0) ? (int)(npairs_k / 8) : 0;
   void* args2[] = {&p2};
   e = hipLaunchKernel(kk.dkdv[v][c], dim3((unsigned)(nblk_k * npairs_k)),
                       dim3((unsigned)kk.dkdv_threads), args2, 0, (hipStream_t)stream);
