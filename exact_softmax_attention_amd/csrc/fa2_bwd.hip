@@ -27,7 +27,7 @@
 // atomics and gives bitwise-reproducible gradients:
 //   fa2_bwd_dq_kernel    rows outer (one workgroup = 128 query rows, 32 per wave), key/value
 //                        tiles inner: S, dP, dS, then dQ += dS K. It also writes D.
-//   fa2_bwd_dkdv_kernel  columns outer (one workgroup = 128 keys of one key/value head, 32 per
+//   fa2_bwd_dkdv_kernel  columns outer (one workgroup = keys of one key/value head, 32 per
 //                        wave), query tiles of every query head of the group inner: S, dP,
 //                        dS, then dV += P^T dO and dK += dS^T Q.
 // S and dP are computed in both (7 matrix products instead of the pages' 5).
@@ -362,9 +362,9 @@ void fa2_bwd_dq_kernel(BwdParams p) {
 
 // ---- dK/dV kernel ----------------------------------------------------------------------
 
-template <int D, int BQ>
+template <int D, int BQ, int NW = 4>
 struct DkvTile {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = NW;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BK = 32 * WAVES;             // keys per workgroup
   static constexpr int ROWB = 2 * D;
@@ -384,10 +384,10 @@ struct DkvTile {
 
 // KLDS: the wave's K rows are kept in LDS (stored once, in the swizzled layout of the Q row
 // reads) instead of 32 registers, which lets d = 128 run two waves per SIMD.
-template <int D, int BQ, bool CAUSAL, bool VARLEN, int OCC, bool KLDS>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(OCC, OCC)))
+template <int D, int BQ, bool CAUSAL, bool VARLEN, int NW, int OCC, bool KLDS>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_bwd_dkdv_kernel(BwdParams p) {
-  using TL = DkvTile<D, BQ>;
+  using TL = DkvTile<D, BQ, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char kst[KLDS ? TL::BK * TL::ROWB : 16];
@@ -636,37 +636,40 @@ struct BwdKernels {
   int dq_br;
   int dq_threads;
   int dkdv_threads;
+  int dkdv_bk;           // keys per dK/dV workgroup
   KernelFn dq[2][2];     // [varlen][causal]
   KernelFn dkdv[2][2];
 };
 
-template <int D, int BC_DQ, int NW_DQ, int OCC_DQ, int OCC_DKDV, int BQ_DKDV, bool KLDS>
+template <int D, int BC_DQ, int NW_DQ, int OCC_DQ, int NW_DKDV, int OCC_DKDV, int BQ_DKDV, bool KLDS>
 BwdKernels make_bwd() {
   BwdKernels k;
   k.dq_bc = BC_DQ;
   k.dq_br = DqTile<D, BC_DQ, NW_DQ>::BR;
   k.dq_threads = DqTile<D, BC_DQ, NW_DQ>::THREADS;
-  k.dkdv_threads = DkvTile<D, BQ_DKDV>::THREADS;
+  k.dkdv_threads = DkvTile<D, BQ_DKDV, NW_DKDV>::THREADS;
+  k.dkdv_bk = DkvTile<D, BQ_DKDV, NW_DKDV>::BK;
   k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false, NW_DQ, OCC_DQ>;
   k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false, NW_DQ, OCC_DQ>;
   k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true, NW_DQ, OCC_DQ>;
   k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true, NW_DQ, OCC_DQ>;
-  k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, false, OCC_DKDV, KLDS>;
-  k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, false, OCC_DKDV, KLDS>;
-  k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, true, OCC_DKDV, KLDS>;
-  k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, true, OCC_DKDV, KLDS>;
+  k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, false, NW_DKDV, OCC_DKDV, KLDS>;
+  k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, false, NW_DKDV, OCC_DKDV, KLDS>;
+  k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, true, NW_DKDV, OCC_DKDV, KLDS>;
+  k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, true, NW_DKDV, OCC_DKDV, KLDS>;
   return k;
 }
 
 const BwdKernels* bwd_kernels(int d) {
-  // <D, dQ key tile, dQ waves, dQ waves per SIMD, dK/dV waves per SIMD, dK/dV query step,
-  //  K rows of dK/dV in LDS>: chosen so each kernel keeps as many waves per SIMD as its
-  //  registers allow (d = 128 dK/dV: 32-query steps and K in LDS bring it from one to two).
-  static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 3, 32, true>();
-  static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 2, 32, true>();
+  // <D, dQ key tile, dQ waves, dQ waves per SIMD, dK/dV waves, dK/dV waves per SIMD, dK/dV
+  //  query step, K rows of dK/dV in LDS>: chosen so each kernel keeps as many waves per SIMD
+  //  as its registers allow (d = 128 dK/dV: 32-query steps and K in LDS bring it from one to
+  //  two).
+  static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 4, 3, 32, true>();
+  static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 4, 2, 32, true>();
   // d = 256: the dQ^T, dK^T and dV^T accumulators are 128 registers each, so both kernels run
   // one wave per SIMD (dK/dV: 129 KB of LDS, one workgroup per CU).
-  static const BwdKernels k256 = make_bwd<256, 32, 4, 1, 1, 32, true>();
+  static const BwdKernels k256 = make_bwd<256, 32, 4, 1, 4, 1, 32, true>();
   return d == 64 ? &k64 : d == 128 ? &k128 : d == 256 ? &k256 : nullptr;
 }
 
@@ -744,7 +747,7 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   if (N == 0) return bwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
   if (st != FA2_OK) return st;
-  const long long nblk = ((long long)N + 127) / 128;
+  const long long nblk = ((long long)N + 127) / 128;   // most blocks any kernel launches
   const long long pq = (long long)B * H, pk = (long long)B * H_kv;
   if (nblk * pq > 0x7fffffffLL || pq * (long long)N > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
   BwdParams p;
@@ -759,7 +762,8 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.T = N;
   const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
   const long long nblk_q = ((long long)N + kk.dq_br - 1) / kk.dq_br;
-  return bwd_launch(kk, false, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
+  const long long nblk_k = ((long long)N + kk.dkdv_bk - 1) / kk.dkdv_bk;
+  return bwd_launch(kk, false, causal != 0, p, (int)nblk_q, (int)nblk_k, pq, pk, stream);
 }
 
 int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -774,7 +778,7 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   if (!aligned_to(cu_seqlens, 4)) return FA2_ERR_MISALIGNED;
   int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
   if (st != FA2_OK) return st;
-  const long long nblk = ((long long)max_seqlen + 127) / 128;
+  const long long nblk = ((long long)max_seqlen + 127) / 128;   // most blocks any kernel launches
   const long long pq = (long long)num_seqs * H, pk = (long long)num_seqs * H_kv;
   if (nblk * pq > 0x7fffffffLL || (long long)H * total_tokens > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
   BwdParams p;
@@ -789,7 +793,8 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   p.T = total_tokens;
   const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
   const long long nblk_q = ((long long)max_seqlen + kk.dq_br - 1) / kk.dq_br;
-  return bwd_launch(kk, true, causal != 0, p, (int)nblk_q, (int)nblk, pq, pk, stream);
+  const long long nblk_k = ((long long)max_seqlen + kk.dkdv_bk - 1) / kk.dkdv_bk;
+  return bwd_launch(kk, true, causal != 0, p, (int)nblk_q, (int)nblk_k, pq, pk, stream);
 }
 
 }  // extern "C"
