@@ -103,6 +103,12 @@ def cpu_baseline(w, q, k, v, heads: int):
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
+def default_warmup(seconds_per_step: float) -> int:
+    """Untimed steps for about WARMUP_SECONDS of work: 5 probe steps, then at least 5 and at
+    most 20000 more."""
+    return 5 + max(5, min(20000, math.ceil(WARMUP_SECONDS / max(seconds_per_step, 1e-6))))
+
+
 def run(args):
     import torch
 
@@ -220,8 +226,7 @@ def run(args):
         for _ in range(4):
             step()
         torch.cuda.synchronize()
-        per_step = (time.perf_counter() - t0) / 4
-        args.warmup = 5 + max(5, min(20000, math.ceil(WARMUP_SECONDS / max(per_step, 1e-6))))
+        args.warmup = default_warmup((time.perf_counter() - t0) / 4)
         for _ in range(args.warmup - 5):
             step()
     else:

@@ -66,3 +66,10 @@ def test_stored_traffic_matches_the_current_kernel_or_is_ignored():
     t = bench.load_traffic()
     if t is not None:
         assert t["fetch_bytes_per_launch"] > 0 and t["write_bytes_per_launch"] > 0
+
+
+def test_default_warmup_covers_about_half_a_second():
+    assert bench.default_warmup(1e-3) == 5 + 500                     # 1 ms steps: ~0.5 s
+    assert bench.default_warmup(0.17e-3) * 0.17e-3 >= bench.WARMUP_SECONDS
+    assert bench.default_warmup(2.0) == 10                           # long steps: at least 10
+    assert bench.default_warmup(0.0) == 5 + 20000                    # bounded for empty steps
