@@ -388,9 +388,9 @@ def main():
         ingest_counters(*args.ingest_counters, steps=args.steps)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the forward shards across GPUs by (batch, head) with no communication; only the "
-              "one-GPU share is built).", file=sys.stderr)
+              "one-GPU share is implemented).", file=sys.stderr)
         sys.exit(2)
     run(args)
 
