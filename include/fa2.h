@@ -222,7 +222,7 @@ int fa2_fwd_geometry(int B, int H, int N, int d, int causal, int variant,
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa2_status_str(int status);
 
-/* Static name of a kernel variant ("d128_br128_bc64" ...), or "" if out of range. */
+/* Static name of a kernel variant (e.g. "d128_w8_bc64_opt_la4"), or "" if out of range. */
 const char* fa2_variant_name(int d, int variant);
 
 /* ABI version of this header; bumped on any incompatible change. */
