@@ -125,6 +125,14 @@ def _check_tensor(name, t, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _same_device(*tensors):
+    """Every tensor of one call must live on the device the kernels are launched on."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"all tensors of a call must be on one device; got {dev} and {t.device}")
+
+
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, variant: int = 0):
     """O, LSE = softmax(scale * q k^T [causal mask]) v for bf16 [B, H, N, d] tensors.
 
@@ -149,6 +157,7 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     _check_tensor("lse", lse, torch.float32, 3)
     if out.shape != q.shape or tuple(lse.shape) != (B, H, N) or out.device != q.device or lse.device != q.device:
         raise ValueError("out/lse shape or device mismatch")
+    _same_device(q, k, v, out, lse)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -184,6 +193,7 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale
     _check_tensor("lse", lse, torch.float32, 2)
     if out.shape != q.shape or tuple(lse.shape) != (H, T):
         raise ValueError("out/lse shape mismatch")
+    _same_device(q, k, v, cu_seqlens, out, lse)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_fwd_varlen_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -220,6 +230,7 @@ def fwd_gqa(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     _check_tensor("lse", lse, torch.float32, 3)
     if out.shape != q.shape or tuple(lse.shape) != (B, H, N) or out.device != q.device or lse.device != q.device:
         raise ValueError("out/lse shape or device mismatch")
+    _same_device(q, k, v, out, lse)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -253,6 +264,7 @@ def fwd_varlen_gqa(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, s
     _check_tensor("lse", lse, torch.float32, 2)
     if out.shape != q.shape or tuple(lse.shape) != (H, T):
         raise ValueError("out/lse shape mismatch")
+    _same_device(q, k, v, cu_seqlens, out, lse)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_fwd_varlen_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -292,6 +304,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     _check_tensor("delta", delta, torch.float32, 3)
     if tuple(delta.shape) != (B, H, N):
         raise ValueError("delta must be [B, H, N]")
+    _same_device(q, k, v, o, lse, dout, dq, dk, dv, delta)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -330,6 +343,7 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool 
     _check_tensor("delta", delta, torch.float32, 2)
     if tuple(delta.shape) != (H, T):
         raise ValueError("delta must be [H, T]")
+    _same_device(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, delta)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -364,6 +378,7 @@ def fwd_chunk(q, k, v, causal: bool = False, diag: int = 0, scale: float | None 
     _check_tensor("lse", lse, torch.float32, 3)
     if out.shape != q.shape or tuple(lse.shape) != (B, H, N_q):
         raise ValueError("out/lse shape mismatch")
+    _same_device(q, k, v, out, lse)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_fwd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -390,6 +405,7 @@ def lse_merge(o_parts, lse_parts, out=None, lse=None):
     _check_tensor("lse", lse, torch.float32, lse.dim())
     if tuple(out.shape) != tuple(o_parts.shape[1:]) or tuple(lse.shape) != tuple(lse_parts.shape[1:]):
         raise ValueError("out/lse shape mismatch")
+    _same_device(o_parts, lse_parts, out, lse)
     lib = load_library()
     with torch.cuda.device(o_parts.device):
         st = lib.fa2_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, rows, d, out.data_ptr(), lse.data_ptr(),
@@ -430,6 +446,7 @@ def fwd_splitkv(q, k, v, num_splits: int, causal: bool = False, diag: int = 0, s
     if out.shape != q.shape or tuple(lse.shape) != (B, H, N_q) or tuple(o_parts.shape) != (S, B, H, N_q, d) \
             or tuple(lse_parts.shape) != (S, B, H, N_q):
         raise ValueError("out/lse/o_parts/lse_parts shape mismatch")
+    _same_device(q, k, v, out, lse, o_parts, lse_parts)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),

@@ -308,3 +308,20 @@ def test_metric_flops():
     # 4*B*H*N^2*d, halved for causal (paper-graph-ui "Evaluation Methodology", Metrics)
     assert metric_flops(1, 16, 16384, 128, True) == 2 * 16 * 16384 ** 2 * 128
     assert metric_flops(8, 16, 2048, 128, False) == 4 * 8 * 16 * 2048 ** 2 * 128
+
+
+def test_binding_rejects_tensors_on_different_devices():
+    import torch
+    a = torch.zeros(2)
+    _lib._same_device(a, torch.zeros(3))                       # one device: fine
+    with pytest.raises(ValueError, match="one device"):
+        _lib._same_device(a, torch.zeros(2, device="meta"))
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa2.fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fa2.bwd(q, q, q, q, torch.zeros(1, 1, 8), q)
