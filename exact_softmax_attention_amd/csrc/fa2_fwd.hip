@@ -962,8 +962,11 @@ int fwd_chunk_impl(const void* q, const void* k, const void* v, void* o, float* 
   const long long wg = tr * nbh;
   // Element offsets are 64-bit in the kernel; the grid and row indices must fit 31 bits.
   if (wg > 0x7fffffffLL || nbh * (long long)N_q > 0x7fffffffLL ||
-      (long long)B * H_kv * (long long)N_k > 0x7fffffffLL)
+      (long long)B * H_kv * (long long)N_k > 0x7fffffffLL || (long long)N_q + N_k + 1024 > 0x7fffffffLL)
     return FA2_ERR_TOO_LARGE;
+  // A causal offset beyond N_k already allows every key and one below -N_q none, so clamping
+  // to [-N_q, N_k] changes no mask and keeps the kernel's 32-bit index sums in range.
+  diag = diag > N_k ? N_k : (diag < -N_q ? -N_q : diag);
   int split_len = N_k, ns = 1;
   if (num_splits > 1 && N_k > 0) {
     if (!o_parts || !lse_parts) return FA2_ERR_NULL_PTR;

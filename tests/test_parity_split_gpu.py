@@ -48,7 +48,8 @@ def test_chunk_small(d, nq, nk):
     scale = 1.0 / np.sqrt(d)
     qn, kn, vn = gen_q.double().numpy(), k.double().numpy(), v.double().numpy()
     for causal in (False, True):
-        for diag in sorted({0, nk - nq, -50, 200}):
+        # +-2^30: the documented extremes (every key allowed / none allowed)
+        for diag in sorted({0, nk - nq, -50, 200, 1 << 30, -(1 << 30)}):
             o_ref, l_ref = attention_chunk(qn, kn, vn, causal, diag, scale)
             for variant in range(fa2.num_variants(d)):
                 print(f"[case] chunk d={d} nq={nq} nk={nk} causal={causal} diag={diag} v{variant}", flush=True)
