@@ -27,7 +27,9 @@
  *   - On success every element of o and lse covered by the call is overwritten (for the
  *     varlen entry: the rows of every sequence, see below). Inputs are never written.
  *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
- *     the call returns without synchronising.
+ *     the call returns without synchronising. A call enqueues kernel launches only (no
+ *     allocation, memset, copy or host synchronisation), so it may be captured in a HIP
+ *     graph and replayed.
  *   - Arguments are validated on the host before any HIP call. On any error nothing is
  *     launched and nothing is written; the return value says why (FA2_* codes below).
  *   - Problems with zero rows (N == 0, total_tokens == 0 or num_seqs == 0) succeed without a
