@@ -18,6 +18,10 @@ Prints ONE JSON line. ``roofline.traffic`` comes from rocprofv3 FETCH_SIZE/WRITE
 counter runs ingested with ``--ingest-counters`` (stored under profiles/ together with the
 hash of the kernel source they were taken on); it is null when the source has changed
 since. ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same workload.
+``launch_ms`` repeats the K steps with one event pair each (median, min, max of single
+launches); ``gpu_clock`` is the shader clock and board power sampled with amd-smi during
+about a second of further untimed steps (null where amd-smi is absent; ``--no-clock`` skips
+it). Neither changes ``value``.
 """
 from __future__ import annotations
 
@@ -36,12 +40,14 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PF)
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0   # the shader clock the published peak is quoted at
 A100_FIG5D_16K_TFLOPS = 197.0   # the pages' FA2 forward, causal, d=128, 16k (A100; context only)
 KERNEL_SRCS = [os.path.join(ROOT, "exact_softmax_attention_amd", "csrc", name) for name in ("fa2_fwd.hip", "fa2_dev.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_long16k_traffic.json")
 WORKLOAD_NAMES = ("single_head_256", "batch8_2k_d128", "batch8_2k_d64_causal", "long_16k_causal", "varlen16_causal")
 COPY_BYTES = 1 << 30   # the calibration copy kernel moves 1 GiB in and 1 GiB out
 WARMUP_SECONDS = 0.5   # default warmup: untimed work before the timed steps, in seconds
+CLOCK_SECONDS = 1.0    # untimed steps after the timed ones while amd-smi samples the shader clock
 
 
 def kernel_source_hash() -> str:
@@ -101,6 +107,71 @@ def cpu_baseline(w, q, k, v, heads: int):
             "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, all {w.N} rows, fp64 numpy "
                       f"({dt:.2f} s; BLAS threads = cores)",
             "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def parse_amdsmi_metric(text: str):
+    """Shader clocks (MHz, one per XCD) and socket power (W) of the first GPU in the JSON
+    printed by ``amd-smi metric -p -c --json``; (None, None) for what is missing."""
+    try:
+        data = json.loads(text)
+    except (ValueError, TypeError):
+        return None, None
+    if isinstance(data, dict):
+        data = data.get("gpu_data", [data])
+    if not isinstance(data, list) or not data or not isinstance(data[0], dict):
+        return None, None
+    gpu = data[0]
+    clocks = []
+    for name, entry in sorted((gpu.get("clock") or {}).items()):
+        clk = entry.get("clk") if isinstance(entry, dict) and name.startswith("gfx") else None
+        if isinstance(clk, dict) and isinstance(clk.get("value"), (int, float)):
+            clocks.append(float(clk["value"]))
+    power = ((gpu.get("power") or {}).get("socket_power") or {}).get("value")
+    return (clocks or None), (float(power) if isinstance(power, (int, float)) else None)
+
+
+def sample_gpu_clock(step, seconds: float = CLOCK_SECONDS):
+    """Run ``step`` back to back for about ``seconds`` while amd-smi samples the shader clocks
+    and the board power. Returns medians over the samples, or None without amd-smi."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    smi = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if smi is None:
+        return None
+    samples, done = [], threading.Event()
+
+    def poll():
+        while not done.is_set():
+            try:
+                r = subprocess.run([smi, "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            clocks, power = parse_amdsmi_metric(r.stdout) if r.returncode == 0 else (None, None)
+            if clocks:
+                samples.append((sum(clocks) / len(clocks), min(clocks), max(clocks), power))
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds or (not samples and time.perf_counter() - t0 < 4 * seconds):
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    done.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    powers = [x[3] for x in samples if x[3] is not None]
+    return {"gfx_mhz_median": med([x[0] for x in samples]), "gfx_mhz_min": min(x[1] for x in samples),
+            "gfx_mhz_max": max(x[2] for x in samples),
+            "socket_power_w_median": med(powers) if powers else None,
+            "samples": len(samples), "source": "amd-smi metric -p -c (mean over XCDs per sample)"}
 
 
 def default_warmup(seconds_per_step: float) -> int:
@@ -243,6 +314,23 @@ def run(args):
     ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
 
+    # The same steps once more, each between its own pair of events on the launch stream:
+    # the spread of single launches (median, min, max), reported beside the mean above.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    single = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    launch_ms = {"median": round(single[len(single) // 2], 5), "min": round(single[0], 5),
+                 "max": round(single[-1], 5), "n": len(single)} if single else None
+    gpu_clock = sample_gpu_clock(step) if args.clock else None
+    if gpu_clock:
+        # the dense peak scaled to the sampled clock (the published peak assumes 2.4 GHz)
+        at_clock = PEAK_BF16_TFLOPS * gpu_clock["gfx_mhz_median"] / PEAK_CLOCK_MHZ
+        gpu_clock.update(peak_at_clock_tflops=round(at_clock, 1), frac_at_clock=round(tflops / at_clock, 4))
+
     def time_fn(fn, reps):
         for _ in range(3):
             fn()
@@ -318,6 +406,8 @@ def run(args):
             "flops_per_launch": flops,
             "kernel_ms": round(ms, 5),
         },
+        "launch_ms": launch_ms,
+        "gpu_clock": gpu_clock,
     }
     if args.cpu_baseline_heads > 0:
         out["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_baseline_heads)
@@ -383,6 +473,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB copy kernel (counter calibration for --ingest-counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--no-clock", dest="clock", action="store_false",
+                    help=f"skip the shader-clock sample (amd-smi, about {CLOCK_SECONDS} s of extra untimed steps)")
     args = ap.parse_args()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, steps=args.steps)

@@ -73,3 +73,18 @@ def test_default_warmup_covers_about_half_a_second():
     assert bench.default_warmup(0.17e-3) * 0.17e-3 >= bench.WARMUP_SECONDS
     assert bench.default_warmup(2.0) == 10                           # long steps: at least 10
     assert bench.default_warmup(0.0) == 5 + 20000                    # bounded for empty steps
+
+
+def test_parse_amdsmi_metric():
+    def gfx(v):
+        return {"clk": {"value": v, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"}}
+    doc = {"gpu_data": [{"gpu": 0, "power": {"socket_power": {"value": 1330, "unit": "W"}},
+                         "clock": {"gfx_0": gfx(1800), "gfx_1": gfx(2000), "mem_0": gfx(2000),
+                                   "gfx_2": {"clk": "N/A"}}}]}
+    clocks, power = bench.parse_amdsmi_metric(json.dumps(doc))
+    assert clocks == [1800.0, 2000.0] and power == 1330.0           # memory clock and N/A skipped
+    # a bare list of GPUs, no power reading
+    clocks, power = bench.parse_amdsmi_metric(json.dumps([{"clock": {"gfx_0": gfx(2100)}}]))
+    assert clocks == [2100.0] and power is None
+    assert bench.parse_amdsmi_metric("not json") == (None, None)
+    assert bench.parse_amdsmi_metric(json.dumps({"gpu_data": []})) == (None, None)
