@@ -8,8 +8,8 @@ The GPU O is bf16, so its own rounding (<= half an ulp, 2^-9 relative) is inside
 Coverage: the five benchmark workloads (the single-head one fully; the others at full size on sampled rows that
 the oracle computes one by one, including row-block edges and the last rows), odd and ragged
 shapes spanning several tiles, every kernel variant, packed variable-length batches with
-empty/1-token/tile-edge sequences, scale edge cases, large score ranges, long sequences,
-determinism and batch invariance.
+empty/1-token/tile-edge sequences, scale edge cases, large score ranges, row maxima that
+move on every key tile (or never), long sequences, determinism and batch invariance.
 """
 import math
 
@@ -172,6 +172,35 @@ def test_large_scores():
         o_ref, l_ref = attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal,
                                  1 / math.sqrt(128))
         _check(_f64(o), _f64(l), o_ref, l_ref, f"scores x16 causal{int(causal)}")
+
+
+@pytest.mark.parametrize("pattern", ["rising", "falling", "zigzag"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_moving_row_max(d, pattern):
+    """Scores built so that the row maximum moves by 10 (in log2 units) with every 64 keys
+    (rising), never moves after the first keys (falling: later tiles underflow), or rises on
+    every other tile (zigzag). The reference max of the optimistic and lazy bookkeeping is
+    then moved and the accumulator rescaled on every tile, or never. All variants against
+    the oracle."""
+    N, scale = 700, 1.0 / math.sqrt(d)
+    c = scale * math.log2(math.e)
+    j = torch.arange(N, dtype=torch.float64)
+    t = j * (10.0 / (64.0 * c))                       # q.k grows by 10/c per 64 keys
+    if pattern == "falling":
+        t = -t
+    elif pattern == "zigzag":
+        t = torch.where((j // 64) % 2 == 0, t, -t)
+    gen = torch.Generator().manual_seed(41 + d)
+    q = (1.0 + 0.05 * torch.randn((1, 2, N, d), generator=gen)).to(torch.bfloat16)
+    k = ((t / d)[None, None, :, None] + 0.01 * torch.randn((1, 2, N, d), generator=gen, dtype=torch.float64))
+    k = k.float().to(torch.bfloat16)
+    v = torch.randn((1, 2, N, d), generator=gen).to(torch.bfloat16)
+    for causal in (False, True):
+        o_ref, l_ref = attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
+        for variant in range(fa2.num_variants(d)):
+            print(f"[case] moving max {pattern} d={d} causal={causal} v{variant}", flush=True)
+            o, l = _run_fixed(q, k, v, causal, scale, variant)
+            _check(_f64(o), _f64(l), o_ref, l_ref, f"{pattern} d{d} causal{int(causal)} v{variant}")
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
