@@ -27,7 +27,23 @@ from ._lib import (
     variant_name,
 )
 
+
+def attention(*args, **kwargs):
+    """Differentiable attention (autograd reaches the library's backward); see
+    ``exact_softmax_attention_amd.autograd.attention``."""
+    from .autograd import attention as _attention
+    return _attention(*args, **kwargs)
+
+
+def attention_varlen(*args, **kwargs):
+    """Differentiable packed variable-length attention; see
+    ``exact_softmax_attention_amd.autograd.attention_varlen``."""
+    from .autograd import attention_varlen as _attention_varlen
+    return _attention_varlen(*args, **kwargs)
+
 __all__ = [
+    "attention",
+    "attention_varlen",
     "FA2_ABI_VERSION",
     "Fa2Error",
     "STATUS",

@@ -316,3 +316,11 @@ def test_binding_rejects_tensors_on_different_devices():
     _lib._same_device(a, torch.zeros(3))                       # one device: fine
     with pytest.raises(ValueError, match="one device"):
         _lib._same_device(a, torch.zeros(2, device="meta"))
+
+
+def test_autograd_wrapper_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    import exact_softmax_attention_amd as fa2
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa2.attention(q, q, q)
