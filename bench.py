@@ -230,7 +230,7 @@ def run(args):
 
     merge_info = None
     if args.split_kv:
-        if w.varlen or args.bwd or args.kv_heads:
+        if w.varlen or args.bwd or args.fwd_bwd or args.kv_heads:
             raise SystemExit("--split-kv runs the forward of a fixed-length MHA workload")
         S, N = args.split_kv, w.N
         nq = args.q_rows or N
@@ -262,9 +262,9 @@ def run(args):
                       "merge_bytes": S * rows * (2 * w.d + 4) + rows * (2 * w.d + 4),
                       "fns": (one_pass, merge_only)}
 
-    if args.bwd:
+    if args.bwd or args.fwd_bwd:
         if w.varlen:
-            raise SystemExit("--bwd runs on fixed-length workloads")
+            raise SystemExit("--bwd / --fwd-bwd run on fixed-length workloads")
         gen = torch.Generator(device="cpu").manual_seed(1000 + w.seed)
         dod = torch.randn(qd.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).to(dev)
         if kd.shape[1] == qd.shape[1]:
@@ -273,10 +273,23 @@ def run(args):
             fa2.fwd_gqa(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
         delta = torch.empty_like(lse)
+        fwd_flops = flops
         flops = 2.5 * flops   # five matrix products against the forward's two
 
         def step():
             fa2.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+
+        if args.fwd_bwd:      # one training step of the attention: the forward, then the backward
+            flops += fwd_flops
+            fwd_step = (lambda: fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                                        variant=args.variant)) if kd.shape[1] == qd.shape[1] else \
+                (lambda: fa2.fwd_gqa(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                                     variant=args.variant))
+            bwd_step = step
+
+            def step():
+                fwd_step()
+                bwd_step()
 
     if args.calib_copy:   # a plain copy kernel of known size, for counter calibration
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -357,7 +370,7 @@ def run(args):
 
     traffic = None
     t = (load_traffic() if (w.name == "long_16k_causal" and args.variant == 0
-                            and not (args.kv_heads or args.bwd or args.split_kv or args.head_dim))
+                            and not (args.kv_heads or args.bwd or args.fwd_bwd or args.split_kv or args.head_dim))
          else None)
     if t is not None:
         traffic = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
@@ -372,12 +385,17 @@ def run(args):
                                    f"{args.kv_heads} key/value heads", "H_kv": args.kv_heads})
     if args.bwd:
         config.update({"workload": f"backward of {config['workload']}", "kernel_variant": "bwd_dq+bwd_dkdv"})
+    if args.fwd_bwd:
+        config.update({"workload": f"forward then backward of {config['workload']}",
+                       "kernel_variant": f"{variant}+bwd_dq+bwd_dkdv"})
     if split_report is not None:
         config.update({"workload": f"split-KV forward ({split_report['parts']} key pieces in one launch + LSE merge), last "
                                    f"{split_report['q_rows']} queries of {config['workload']}",
                        "split_kv": split_report})
     out = {
         "metric": ("attention bwd TFLOP/s (2.5 x 4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak" if args.bwd
+                   else "attention fwd+bwd TFLOP/s (3.5 x 4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak"
+                   if args.fwd_bwd
                    else "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) + % of bf16 MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
@@ -388,7 +406,8 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3)
-                        if w.name == "long_16k_causal" and not (args.kv_heads or args.bwd or args.split_kv or args.head_dim)
+                        if w.name == "long_16k_causal"
+                        and not (args.kv_heads or args.bwd or args.fwd_bwd or args.split_kv or args.head_dim)
                         else None),
         "dtype": "bf16",
         "data": "synthetic",
@@ -402,6 +421,8 @@ def run(args):
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_bytes": (bwd_algorithmic_bytes(w, args.kv_heads or None) if args.bwd
+                                  else algorithmic_bytes(w, lengths, args.kv_heads or None)
+                                  + bwd_algorithmic_bytes(w, args.kv_heads or None) if args.fwd_bwd
                                   else algorithmic_bytes(w, lengths, args.kv_heads or None)),
             "flops_per_launch": flops,
             "kernel_ms": round(ms, 5),
@@ -411,7 +432,8 @@ def run(args):
     }
     if args.cpu_baseline_heads > 0:
         out["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_baseline_heads)
-                               if not (w.varlen or args.kv_heads or args.bwd or args.split_kv or args.head_dim)
+                               if not (w.varlen or args.kv_heads or args.bwd or args.fwd_bwd or args.split_kv
+                                       or args.head_dim)
                                else None)
     print(json.dumps(out), flush=True)
 
@@ -460,6 +482,8 @@ def main():
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (dQ, dK, dV from dO, O, LSE) instead of the forward")
+    ap.add_argument("--fwd-bwd", action="store_true",
+                    help="time the forward followed by the backward (one attention training step)")
     ap.add_argument("--split-kv", type=int, default=0,
                     help="split the keys into this many pieces in one launch and merge them (fa2_fwd_splitkv)")
     ap.add_argument("--q-rows", type=int, default=0,
@@ -479,6 +503,8 @@ def main():
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, steps=args.steps)
         return
+    if args.bwd and args.fwd_bwd:
+        ap.error("--bwd and --fwd-bwd are exclusive")
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the forward shards across GPUs by (batch, head) with no communication; only the "

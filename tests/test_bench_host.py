@@ -88,3 +88,9 @@ def test_parse_amdsmi_metric():
     assert clocks == [2100.0] and power is None
     assert bench.parse_amdsmi_metric("not json") == (None, None)
     assert bench.parse_amdsmi_metric(json.dumps({"gpu_data": []})) == (None, None)
+
+
+def test_bwd_and_fwd_bwd_are_exclusive():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--bwd", "--fwd-bwd"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "exclusive" in r.stderr
