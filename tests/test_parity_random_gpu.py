@@ -16,7 +16,6 @@ row, and two roundings each reach 2^-9 * |V|: the bf16 P~ in the numerator again
 fp32 row sum, and O's own bf16 rounding. With max |V| near 4.8 that is 1.9e-2, and the worst
 draw measures 1.85e-2.
 """
-import math
 
 import numpy as np
 import pytest
