@@ -317,11 +317,30 @@ def run(args):
         for _ in range(args.warmup):
             step()
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # The K steps captured once in a HIP graph (every entry point only enqueues kernel
+        # launches), so the timed region is one graph launch: no per-step host overhead.
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        graph.replay()                    # one untimed replay
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -378,6 +397,8 @@ def run(args):
     variant = fa2.variant_name(w.d, args.variant)
     config = {"workload": f"{w.name}: {w.description}", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
               "causal": w.causal, "kernel_variant": variant}
+    if args.graph:
+        config["timing"] = f"{args.steps} steps captured in one HIP graph, one replay timed"
     if w.varlen:
         config.update({"lengths": lengths, "total_tokens": sum(lengths)})
     if args.kv_heads:
@@ -482,6 +503,8 @@ def main():
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (dQ, dK, dV from dO, O, LSE) instead of the forward")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K steps as one captured HIP graph (no per-launch host overhead)")
     ap.add_argument("--fwd-bwd", action="store_true",
                     help="time the forward followed by the backward (one attention training step)")
     ap.add_argument("--split-kv", type=int, default=0,
