@@ -82,6 +82,44 @@ def test_full_size_sampled(name):
         _check(_f64(o[b, h, rows]), _f64(l[b, h, rows]), o_ref, l_ref, f"{name} b{b} h{h} {len(rows)} rows")
 
 
+@pytest.mark.parametrize("name", ["batch8_2k_d128", "batch8_2k_d64_causal", "long_16k_causal"])
+def test_full_size_every_variant_sampled(name):
+    """Every kernel variant at the benchmark sizes, on rows sampled from one (batch, head)
+    pair (the first, the last row-block edges and random rows)."""
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    rng = np.random.default_rng(200 + w.seed)
+    b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+    rows = _sample_rows(w.N, rng, extra=8)
+    o_ref, l_ref = attention_rows(q[b, h].double().numpy(), k[b, h].double().numpy(), v[b, h].double().numpy(),
+                                  w.causal, w.scale, rows)
+    for variant in range(fa2.num_variants(w.d)):
+        print(f"[case] {name} v{variant} ({fa2.variant_name(w.d, variant)})", flush=True)
+        o, l = fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, variant=variant)
+        torch.cuda.synchronize()
+        _check(_f64(o[b, h, rows]), _f64(l[b, h, rows]), o_ref, l_ref, f"{name} v{variant} b{b} h{h}")
+
+
+def test_varlen16_every_variant_sampled():
+    w = WORKLOADS["varlen16_causal"]
+    q, k, v, cu, lengths = workload_inputs(w)
+    qd, kd, vd, cud = q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV)
+    rng = np.random.default_rng(106)
+    s = int(np.argmax(lengths))
+    a, e = int(cu[s]), int(cu[s + 1])
+    h = int(rng.integers(w.H))
+    rows = _sample_rows(e - a, rng, extra=8)
+    o_ref, l_ref = attention_rows(q[h, a:e].double().numpy(), k[h, a:e].double().numpy(), v[h, a:e].double().numpy(),
+                                  True, w.scale, rows)
+    idx = [a + r for r in rows]
+    for variant in range(fa2.num_variants(w.d)):
+        print(f"[case] varlen16 v{variant}", flush=True)
+        o, l = fa2.fwd_varlen(qd, kd, vd, cud, max(lengths), causal=True, scale=w.scale, variant=variant)
+        torch.cuda.synchronize()
+        _check(_f64(o[h, idx]), _f64(l[h, idx]), o_ref, l_ref, f"varlen16 v{variant} seq{s} h{h}")
+
+
 def test_varlen16_sampled():
     w = WORKLOADS["varlen16_causal"]
     q, k, v, cu, lengths = workload_inputs(w)
