@@ -195,6 +195,9 @@ def run(args):
                                 description=w.description.replace(f"d={w.d}", f"d={args.head_dim}"))
     dev = torch.device("cuda:0")
     lengths = None
+    # The default kernel is timed through the C ABI's plain entry points (fa2_fwd,
+    # fa2_fwd_varlen); another variant through the *_variant calls.
+    entry_variant = None if args.variant == 0 else args.variant
     if w.varlen:
         q, k, v, cu, lengths = workload_inputs(w)
         qd, kd, vd, cud = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
@@ -205,7 +208,7 @@ def run(args):
 
         def step():
             fa2.fwd_varlen(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o, lse=lse,
-                           variant=args.variant)
+                           variant=entry_variant)
     elif args.kv_heads:
         from synthetic import make_qkv
         if w.H % args.kv_heads:
@@ -226,7 +229,7 @@ def run(args):
         flops = metric_flops(w.B, w.H, w.N, w.d, w.causal)
 
         def step():
-            fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, variant=args.variant)
+            fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, variant=entry_variant)
 
     merge_info = None
     if args.split_kv:

@@ -133,11 +133,13 @@ def _same_device(*tensors):
             raise ValueError(f"all tensors of a call must be on one device; got {dev} and {t.device}")
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, variant: int = 0):
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+        variant: int | None = None):
     """O, LSE = softmax(scale * q k^T [causal mask]) v for bf16 [B, H, N, d] tensors.
 
     Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N]); ``out``/``lse`` may be given
-    preallocated. Enqueued on torch's current stream of q's device.
+    preallocated. Enqueued on torch's current stream of q's device. Without ``variant`` the
+    call goes to ``fa2_fwd`` (the default kernel); with one, to ``fa2_fwd_variant``.
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -160,18 +162,24 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     _same_device(q, k, v, out, lse)
     lib = load_library()
     with torch.cuda.device(q.device):
-        st = lib.fa2_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                 B, H, N, d, int(bool(causal)), float(scale), int(variant), _stream_ptr(q.device))
+        if variant is None:
+            st = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             B, H, N, d, int(bool(causal)), float(scale), _stream_ptr(q.device))
+        else:
+            st = lib.fa2_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                     B, H, N, d, int(bool(causal)), float(scale), int(variant),
+                                     _stream_ptr(q.device))
     _check(st)
     return out, lse
 
 
 def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
-               out=None, lse=None, variant: int = 0):
+               out=None, lse=None, variant: int | None = None):
     """Packed variable-length forward over bf16 [H, T, d] tensors.
 
     ``cu_seqlens`` is an int32 GPU tensor [num_seqs + 1]; sequence s owns tokens
-    [cu[s], cu[s+1]). Returns (o bf16 [H, T, d], lse fp32 [H, T]).
+    [cu[s], cu[s+1]). Returns (o bf16 [H, T, d], lse fp32 [H, T]). Without ``variant`` the
+    call goes to ``fa2_fwd_varlen``; with one, to ``fa2_fwd_varlen_variant``.
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -196,9 +204,15 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale
     _same_device(q, k, v, cu_seqlens, out, lse)
     lib = load_library()
     with torch.cuda.device(q.device):
-        st = lib.fa2_fwd_varlen_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                        cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, d,
-                                        int(bool(causal)), float(scale), int(variant), _stream_ptr(q.device))
+        if variant is None:
+            st = lib.fa2_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, d,
+                                    int(bool(causal)), float(scale), _stream_ptr(q.device))
+        else:
+            st = lib.fa2_fwd_varlen_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                            lse.data_ptr(), cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H,
+                                            d, int(bool(causal)), float(scale), int(variant),
+                                            _stream_ptr(q.device))
     _check(st)
     return out, lse
 

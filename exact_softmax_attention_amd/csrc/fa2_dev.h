@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, t);
 }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (one v_dot2 with (1, 1)): the two bf16 values
+// are exact in fp32, so this sums the weights exactly as the matrix cores will see them.
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one2, acc, false);
+}
+
 // One direct global->LDS load of 16 bytes per lane: lane l's bytes at base + voff land at
 // LDS address lds + 16*l. base and lds are wave-uniform. Completion is tracked by vmcnt,
 // which the caller waits on explicitly before the barrier that publishes the tile.

@@ -305,7 +305,8 @@ void fa2_fwd_kernel(Params p) {
 #pragma unroll
   for (int db = 0; db < TL::NDB; ++db) oacc[db] = (f32x16){};
   float m_run = -INFINITY;  // reference max of S·c (base-2 domain) for this lane's query
-  float l_run = 0.f;        // this lane's partial sum (its half of the keys)
+  float l_run = 0.f;        // this lane's partial sum of P~ in fp32 (its half of the keys): LSE
+  float lb_run = 0.f;       // the same sum over P~ as rounded to bf16 for the MFMA: O's divisor
 
   auto compute_tile = [&](int j, const unsigned char* stage) {
     const int key0 = j * BC;
@@ -355,10 +356,15 @@ void fa2_fwd_kernel(Params p) {
     }
 
     // ---- a6: online softmax (fp32) --------------------------------------------------
-    // pw[c] holds P~ for PV contraction step c as 4 packed bf16 pairs.
+    // pw[c] holds P~ for PV contraction step c as 4 packed bf16 pairs. Two row sums are
+    // kept: the fp32 sum of P~ (for the LSE) and the sum of P~ as rounded to bf16, i.e.
+    // of exactly the weights the PV product consumes, so that O = O~ / l is a normalised
+    // average of V rows even where one key dominates a row.
     u32x4 pw[TL::NPC];
+    float rsb;   // the bf16-rounded sum of the last form_p
     auto form_p = [&](float m_ref) {
       float rsum = 0.f;
+      rsb = 0.f;
 #pragma unroll
       for (int c = 0; c < TL::NPC; ++c) {
         const int kb = c >> 1, r0 = (c & 1) * 8;
@@ -370,6 +376,8 @@ void fa2_fwd_kernel(Params p) {
         }
         pw[c] = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                         pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) rsb = sum_bf16x2(pw[c][w], rsb);
       }
       return rsum;
     };
@@ -386,6 +394,7 @@ void fa2_fwd_kernel(Params p) {
       const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);   // 0 when m_run = -inf
       l_run *= alpha;
+      lb_run *= alpha;
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
       m_run = m_new;
@@ -409,6 +418,7 @@ void fa2_fwd_kernel(Params p) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
       const bool grew = m_new > m_run;
       l_run *= alpha;
+      lb_run *= alpha;
       // Skip the O~ rescale when no row of the wave changed its max (alpha == 1 exactly).
       if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
@@ -418,6 +428,7 @@ void fa2_fwd_kernel(Params p) {
       rs = form_p(m_ref);
     }
     l_run += rs;
+    lb_run += rsb;
 
     // ---- a7: O~^T += V_j^T P~^T -----------------------------------------------------
 #pragma unroll
@@ -463,9 +474,11 @@ void fa2_fwd_kernel(Params p) {
   }
 
   // ---- a8: epilogue: O = O~ / l, LSE = (m + log2 l) ln 2 --------------------------------
+  // O divides by the sum of the bf16 weights the PV product used; the LSE takes the fp32 sum.
   const float l_tot = halves_sum(l_run);
+  const float lb_tot = halves_sum(lb_run);
   if (qrow < seq_len) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
     uint16_t* orow = p.o + (orow0 + (size_t)qrow) * dg;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
@@ -649,7 +662,8 @@ void fa2_fwd_kernel_pp(Params p) {
 #pragma unroll
   for (int db = 0; db < TL::NDB; ++db) oacc[db] = (f32x16){};
   float m_run = -INFINITY;
-  float l_run = 0.f;
+  float l_run = 0.f;      // fp32 sum of P~ (LSE)
+  float lb_run = 0.f;     // sum of P~ as rounded to bf16 (O's divisor)
   f32x16 s[TL::NKB];      // S of the tile the next VALU phase works on
   u32x4 pw[TL::NPC];      // P~ (bf16 pairs) of the tile the next MFMA phase multiplies
 
@@ -736,12 +750,13 @@ void fa2_fwd_kernel_pp(Params p) {
       const float m_new = need ? mt : m_run;
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // 0 if m_run = -inf
       l_run *= alpha;
+      lb_run *= alpha;
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
     const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-    float rsum = 0.f;
+    float rsum = 0.f, rsb = 0.f;
 #pragma unroll
     for (int c = 0; c < TL::NPC; ++c) {
       const int kb = c >> 1, r0 = (c & 1) * 8;
@@ -753,8 +768,11 @@ void fa2_fwd_kernel_pp(Params p) {
       }
       pw[c] = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                       pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) rsb = sum_bf16x2(pw[c][w], rsb);
     }
     l_run += rsum;
+    lb_run += rsb;
   };
 
   // ---- the phase loop ------------------------------------------------------------------
@@ -783,8 +801,9 @@ void fa2_fwd_kernel_pp(Params p) {
 
   // ---- a8: epilogue ------------------------------------------------------------------
   const float l_tot = halves_sum(l_run);
+  const float lb_tot = halves_sum(lb_run);
   if (qrow < seq_len) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
     uint16_t* orow = p.o + (orow0 + (size_t)qrow) * dg;
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db)
@@ -1027,7 +1046,7 @@ const char* fa2_status_str(int status) {
     case FA2_ERR_NULL_PTR: return "a required pointer is NULL";
     case FA2_ERR_BAD_SHAPE: return "bad shape (B, H must be > 0, N >= 0; varlen sizes consistent)";
     case FA2_ERR_UNSUPPORTED_HEADDIM:
-      return "unsupported head dimension (a multiple of 8 up to 256 forward, up to 128 backward)";
+      return "unsupported head dimension (a multiple of 8 from 8 to 256, forward and backward)";
     case FA2_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 B, lse 4 B)";
     case FA2_ERR_BAD_SCALE: return "scale is not finite";
     case FA2_ERR_NO_DEVICE: return "no usable HIP device";

@@ -11,10 +11,12 @@ are small enough for the oracle to finish in seconds; larger shapes are covered 
 fixed parity tests.
 
 The largest O errors come from draws with a large scale and head dimension (score spread
-about 6), where a row's softmax is dominated by one key. O is then close to that key's V
-row, and two roundings each reach 2^-9 * |V|: the bf16 P~ in the numerator against the
-fp32 row sum, and O's own bf16 rounding. With max |V| near 4.8 that is 1.9e-2, and the worst
-draw measures 1.85e-2.
+about 6), where a row's softmax is dominated by one key and O is close to that key's V row.
+The kernel divides O by the sum of the bf16 weights the PV product actually consumed, so the
+rounding of the dominant weight cancels; what remains is O's own bf16 rounding (half an ulp,
+up to 2^-8 relative: 1.6e-2 for |O| just under 8, 7.8e-3 under 4) and the rounding of the
+small weights. Before that normalisation the bf16 dominant weight against an fp32 row sum
+added up to 2^-8 * |V| more, and this sweep's worst draw measured 1.85e-2.
 """
 
 import numpy as np

@@ -4,8 +4,8 @@ The chunk call is compared with oracle.attention_chunk (rows with no allowed key
 back as O = 0 and LSE = -inf exactly); the merge kernel with oracle.lse_merge on the same
 bf16/fp32 inputs; and split-KV end to end (chunks, then merge) with the oracle's full
 attention and with the one-pass forward. Tolerances are the forward's (O max 2e-2, mean
-2e-3; LSE 1e-3): a merged O carries the bf16 rounding of each part (<= 2^-9 relative) plus
-its own.
+2e-3; LSE 1e-3): a merged O carries the bf16 rounding of each part (half an ulp, <= 2^-8
+relative) plus its own.
 """
 import numpy as np
 import pytest
