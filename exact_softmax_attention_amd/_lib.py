@@ -19,7 +19,10 @@ STATUS = {
     7: "FA2_ERR_LAUNCH",
     8: "FA2_ERR_BAD_VARIANT",
     9: "FA2_ERR_TOO_LARGE",
+    10: "FA2_ERR_SCRATCH_TOO_SMALL",
 }
+
+FA2_STATIC_SCRATCH_BYTES = 32 << 20
 
 _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int
@@ -35,6 +38,7 @@ _SIGNATURES = {
     "fa2_fwd_chunk": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p], _c_int),
     "fa2_fwd_splitkv": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p, _c_void_p, _c_int,
                                                             _c_void_p], _c_int),
+    "fa2_fwd_splitkv_noalloc": ([_c_void_p] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_int, _c_void_p], _c_int),
     "fa2_lse_merge": ([_c_void_p, _c_void_p, _c_int, ctypes.c_longlong, _c_int, _c_void_p, _c_void_p, _c_void_p],
                       _c_int),
     "fa2_bwd": ([_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),

@@ -52,6 +52,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa2.h"
 #include "fa2_dev.h"
 
@@ -961,13 +963,26 @@ void fill_scale(Params& p, float scale) {
 
 int heads_per_xcd(long long nbh) { return (nbh % 8 == 0) ? (int)(nbh / 8) : 0; }
 
+// Keys per split-KV piece (a multiple of the variant's key tile) and the number of pieces.
+void split_pieces(int N_k, int num_splits, int bc, int* split_len, int* ns) {
+  *split_len = N_k;
+  *ns = 1;
+  if (num_splits > 1 && N_k > 0) {
+    const int per = (N_k + num_splits - 1) / num_splits;
+    *split_len = (per + bc - 1) / bc * bc;
+    *ns = (N_k + *split_len - 1) / *split_len;
+  }
+}
+
 // Shared body of fa2_fwd_chunk (num_splits == 1) and fa2_fwd_splitkv. With splits, the keys are
 // cut into ns contiguous pieces of split_len keys (a multiple of the key tile), one launch
 // computes every (row block, piece) pair into the caller's o_parts / lse_parts, and the LSE
 // merge combines the pieces into o / lse.
+// With dry_run the call stops after validation, before any HIP call.
 int fwd_chunk_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int H_kv, int N_q, int N_k, int d, int causal, int diag, float scale,
-                   int variant, int num_splits, void* o_parts, float* lse_parts, void* stream) {
+                   int variant, int num_splits, void* o_parts, float* lse_parts, void* stream,
+                   bool dry_run = false) {
   if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N_q < 0 || N_k < 0)
     return FA2_ERR_BAD_SHAPE;
   if (diag < -(1 << 30) || diag > (1 << 30)) return FA2_ERR_BAD_SHAPE;
@@ -991,9 +1006,7 @@ int fwd_chunk_impl(const void* q, const void* k, const void* v, void* o, float* 
     if (!o_parts || !lse_parts) return FA2_ERR_NULL_PTR;
     if (!aligned(o_parts, 16) || !aligned(lse_parts, 4)) return FA2_ERR_MISALIGNED;
     if (num_splits > 65535) return FA2_ERR_TOO_LARGE;
-    const int per = (N_k + num_splits - 1) / num_splits;
-    split_len = (per + var->bc - 1) / var->bc * var->bc;
-    ns = (N_k + split_len - 1) / split_len;
+    split_pieces(N_k, num_splits, var->bc, &split_len, &ns);
   }
   Params p;
   p.q = (const uint16_t*)q;
@@ -1016,9 +1029,40 @@ int fwd_chunk_impl(const void* q, const void* k, const void* v, void* o, float* 
   p.tr = (int)tr;
   p.heads_per_xcd = heads_per_xcd(nbh);
   fill_scale(p, scale);
+  if (dry_run) return FA2_OK;
   st = launch(*var, false, causal != 0, p, (int)wg, stream, ns);
   if (st != FA2_OK || ns == 1) return st;
   return fa2_lse_merge(o_parts, lse_parts, ns, nbh * N_q, d, o, lse, stream);
+}
+
+}  // namespace
+
+// Static scratch of fa2_fwd_splitkv_noalloc: the per-piece partial O and LSE live here instead
+// of in caller workspace. Every device the library runs on holds its own copy until the
+// process ends. Host code must never pass the array's name to a kernel (on the host it is a
+// stand-in, not a device address): the device address comes from hipGetSymbolAddress, once
+// per device, and is kept in scratch_ptr below.
+static __device__ __align__(256) unsigned char scratch[FA2_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's copy of `scratch` (looked up on the first call on that device, with
+// that device current).
+int current_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA2_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA2_ERR_NO_DEVICE;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return FA2_OK;
 }
 
 }  // namespace
@@ -1053,6 +1097,8 @@ const char* fa2_status_str(int status) {
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     case FA2_ERR_BAD_VARIANT: return "kernel variant out of range";
     case FA2_ERR_TOO_LARGE: return "problem too large (grid or index overflow)";
+    case FA2_ERR_SCRATCH_TOO_SMALL:
+      return "split-KV partials exceed the library's static scratch (FA2_STATIC_SCRATCH_BYTES per device)";
     default: return "unknown status";
   }
 }
@@ -1089,6 +1135,35 @@ int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float*
   if (num_splits < 1) return FA2_ERR_BAD_SHAPE;
   return fwd_chunk_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, causal, diag, scale, variant,
                         num_splits, o_parts, lse_parts, stream);
+}
+
+int fa2_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                            int H, int H_kv, int N_q, int N_k, int d, int causal, int diag, float scale,
+                            int num_splits, int variant, void* stream) {
+  if (num_splits < 1) return FA2_ERR_BAD_SHAPE;
+  // Every argument is validated before any HIP call; the workspace stand-ins (o, lse) only
+  // have to be non-null and aligned for this dry run.
+  const int st0 = fwd_chunk_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, causal, diag, scale, variant,
+                                 num_splits, o, lse, stream, true);
+  if (st0 != FA2_OK || N_q == 0) return st0;
+  int count = 0;
+  const Variant* vs = variants_for(padded_dim(d), &count);
+  int split_len = N_k, ns = 1;
+  split_pieces(N_k, num_splits, vs[variant].bc, &split_len, &ns);
+  if (ns == 1)   // one piece (or no keys): the plain chunk call, no scratch
+    return fwd_chunk_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, causal, diag, scale, variant, 1,
+                          nullptr, nullptr, stream);
+  // Partial O [ns, rows, d] bf16, then partial LSE [ns, rows] fp32 at a 256-byte boundary.
+  const unsigned long long rows = (unsigned long long)B * (unsigned long long)H * (unsigned long long)N_q;
+  const unsigned long long obytes = ((unsigned long long)ns * rows * 2ull * (unsigned long long)d + 255ull) & ~255ull;
+  const unsigned long long need = obytes + (unsigned long long)ns * rows * 4ull;
+  if (need > (unsigned long long)FA2_STATIC_SCRATCH_BYTES) return FA2_ERR_SCRATCH_TOO_SMALL;
+  void* base = nullptr;
+  const int st = current_scratch(&base);
+  if (st != FA2_OK) return st;
+  unsigned char* b = (unsigned char*)base;
+  return fwd_chunk_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, causal, diag, scale, variant,
+                        num_splits, b, (float*)(b + obytes), stream);
 }
 
 int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

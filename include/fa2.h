@@ -24,6 +24,8 @@
  *     words (bfloat16 bit patterns). q, k, v, o must be 16-byte aligned; lse 4-byte aligned.
  *   - Ownership: the caller allocates and frees every buffer. The library never allocates,
  *     frees or retains a pointer, and keeps no mutable global state; calls are reentrant.
+ *     (The one exception is fa2_fwd_splitkv_noalloc, which keeps its partials in a static
+ *     device array of the library; see there.)
  *   - On success every element of o and lse covered by the call is overwritten (for the
  *     varlen entry: the rows of every sequence, see below). Inputs are never written.
  *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
@@ -54,8 +56,13 @@ enum fa2_status {
   FA2_ERR_NO_DEVICE = 6,           /* no usable HIP device is current */
   FA2_ERR_LAUNCH = 7,              /* the kernel launch failed (HIP error) */
   FA2_ERR_BAD_VARIANT = 8,         /* variant index out of range for this d */
-  FA2_ERR_TOO_LARGE = 9            /* the grid or an index would overflow 31 bits */
+  FA2_ERR_TOO_LARGE = 9,           /* the grid or an index would overflow 31 bits */
+  FA2_ERR_SCRATCH_TOO_SMALL = 10   /* fa2_fwd_splitkv_noalloc: the partials exceed the
+                                      static scratch (FA2_STATIC_SCRATCH_BYTES) */
 };
+
+/* Size of the static device scratch that fa2_fwd_splitkv_noalloc uses (per device). */
+#define FA2_STATIC_SCRATCH_BYTES (32u << 20)
 
 /*
  * Fixed-length forward.
@@ -159,6 +166,29 @@ int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int H_kv, int N_q, int N_k, int d, int causal, int diag,
                     float scale, int num_splits, void* o_parts, float* lse_parts, int variant,
                     void* stream);
+
+/*
+ * fa2_fwd_splitkv without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The per-piece partial O and LSE live in a static device array of the library,
+ * FA2_STATIC_SCRATCH_BYTES per device (each device the library runs on holds its own copy
+ * until the process ends). The call allocates nothing and frees nothing.
+ *   Arguments, results and validation as fa2_fwd_splitkv (minus o_parts / lse_parts).
+ *   The pieces need P * B * H * N_q * (2 d + 4) bytes (P pieces, the bf16 part rounded up to
+ *   256 bytes); above FA2_STATIC_SCRATCH_BYTES the call returns FA2_ERR_SCRATCH_TOO_SMALL and
+ *   launches nothing. With one piece (num_splits == 1, or N_k == 0) it is fa2_fwd_chunk and
+ *   the scratch is not used.
+ *   The first call on a device looks up that device's copy of the array (hipGetSymbolAddress,
+ *   with the device current); FA2_ERR_NO_DEVICE if that fails.
+ *   Every call on one device shares that device's scratch, which keeps the last call's
+ *   partials (every partial row read by the merge is written by the same call first, so
+ *   nothing needs clearing). Calls that overlap on one device (two streams, or two host
+ *   threads, before the first has finished on the GPU) race on the scratch and may return
+ *   wrong results: serialise them.
+ */
+int fa2_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int N_q, int N_k, int d, int causal,
+                            int diag, float scale, int num_splits, int variant, void* stream);
 
 /*
  * Merge of partial results by their logsumexp (the "LSE mix"):

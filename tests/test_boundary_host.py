@@ -315,6 +315,33 @@ def test_splitkv_workspace_unused_without_split():
     assert _splitkv(Nk=0, k=None, v=None, op=None, lp=None) == 6
 
 
+def _noalloc(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, H_kv=2, Nq=16, Nk=640, d=128, causal=1, diag=0,
+             scale=0.088, S=4, variant=0):
+    return fa2.load_library().fa2_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, causal, diag, scale,
+                                                      S, variant, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(S=0), 2), (dict(S=-3), 2), (dict(H_kv=3), 2), (dict(Nq=-1), 2), (dict(q=None), 1), (dict(lse=None), 1),
+    (dict(d=81), 3), (dict(d=512), 3), (dict(o=FAKE + 2), 4), (dict(lse=FAKE + 1), 4),
+    (dict(scale=float("nan")), 5), (dict(variant=50), 8), (dict(S=70000), 9),
+    # 8 pieces of 32 x 4096 rows at d = 128 need 8 * 131072 * 260 B = 260 MiB > 32 MiB
+    (dict(H=32, H_kv=32, Nq=4096, Nk=8192, S=8), 10),
+])
+def test_noalloc_validation(kwargs, code):
+    """fa2_fwd_splitkv_noalloc returns the header's codes before any HIP call, including
+    FA2_ERR_SCRATCH_TOO_SMALL when the partials would not fit the static scratch."""
+    assert _noalloc(**kwargs) == code
+
+
+def test_noalloc_scratch_rule():
+    # the limit is the header's FA2_STATIC_SCRATCH_BYTES; one piece needs no scratch at all
+    header = open(HEADER).read()
+    assert "#define FA2_STATIC_SCRATCH_BYTES (32u << 20)" in header
+    assert _lib.FA2_STATIC_SCRATCH_BYTES == 32 << 20
+    assert _noalloc(Nq=0, q=None, k=None, v=None, o=None, lse=None) == 0
+
+
 def _merge(op=FAKE, lp=FAKE, S=2, rows=100, d=128, o=FAKE, lse=FAKE):
     return fa2.load_library().fa2_lse_merge(op, lp, S, rows, d, o, lse, None)
 
@@ -366,6 +393,8 @@ def test_no_device_reported():
     assert _chunk() == 6
     assert _merge() == 6
     assert _splitkv() == 6
+    assert _noalloc() == 6
+    assert _noalloc(S=1) == 6
 
 
 def test_binding_rejects_cpu_tensors():

@@ -1,0 +1,71 @@
+"""fa2_fwd_splitkv_noalloc (the split-KV forward with its partials in the library's static
+device scratch, for callers that cannot allocate) against fa2_fwd_splitkv with a caller
+workspace, through the C ABI: two calls in a row, the second with a smaller input, each
+bitwise equal to the workspace call (same kernels, same pieces) and within the forward's
+tolerances of the fp64 oracle; a call whose partials exceed the scratch is refused.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_softmax_attention_amd as fa2
+from exact_softmax_attention_amd._lib import FA2_STATIC_SCRATCH_BYTES
+from oracle import attention_chunk
+from synthetic import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+def _noalloc(q, k, v, S, causal, diag, scale, out, lse):
+    lib = fa2.load_library()
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    return lib.fa2_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                       B, H, H_kv, Nq, Nk, d, int(causal), int(diag), float(scale), int(S), 0,
+                                       int(torch.cuda.current_stream().cuda_stream))
+
+
+@pytest.mark.parametrize("shape", [
+    # (B, H, H_kv, N_q, N_k, d, causal, S): a large call, then a smaller one
+    [(2, 8, 2, 128, 8192, 128, True, 16), (1, 4, 4, 17, 1000, 64, False, 3)],
+    [(1, 16, 16, 64, 16384, 256, True, 8), (1, 2, 1, 5, 333, 96, True, 4)],
+])
+def test_noalloc_matches_workspace_call(shape):
+    for i, (B, H, H_kv, Nq, Nk, d, causal, S) in enumerate(shape):
+        print(f"[case] noalloc call {i}: B{B} H{H}/{H_kv} Nq{Nq} Nk{Nk} d{d} causal={causal} S={S}", flush=True)
+        q, _, _ = make_qkv(B, H, Nq, d, seed=500 + i)
+        _, k, v = make_qkv(B, H_kv, Nk, d, seed=600 + i)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        diag = Nk - Nq
+        scale = 1.0 / np.sqrt(d)
+        o = torch.full_like(qd, float("nan"))
+        l = torch.full((B, H, Nq), float("nan"), device=DEV)
+        st = _noalloc(qd, kd, vd, S, causal, diag, scale, o, l)
+        assert st == 0, fa2.load_library().fa2_status_str(st)
+        o_ws, l_ws = fa2.fwd_splitkv(qd, kd, vd, S, causal=causal, diag=diag, scale=scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ws) and torch.equal(l, l_ws), "differs from the workspace call"
+        o_ref, l_ref = attention_chunk(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, diag,
+                                       scale)
+        err = np.abs(o.float().cpu().double().numpy() - o_ref)
+        lerr = np.abs(l.cpu().double().numpy() - l_ref)
+        print(f"[parity] noalloc call {i}: O max {err.max():.3e} mean {err.mean():.3e} LSE max {lerr.max():.3e}",
+              flush=True)
+        assert err.max() <= O_MAX and err.mean() <= O_MEAN and lerr.max() <= LSE_MAX
+
+
+def test_noalloc_refuses_partials_beyond_the_scratch():
+    B, H, Nq, Nk, d, S = 1, 32, 4096, 8192, 128, 8
+    assert S * B * H * Nq * (2 * d + 4) > FA2_STATIC_SCRATCH_BYTES
+    q, k, v = make_qkv(1, 1, 8, d, seed=7)
+    qd = torch.zeros((B, H, Nq, d), dtype=torch.bfloat16, device=DEV)
+    kd = torch.zeros((B, H, Nk, d), dtype=torch.bfloat16, device=DEV)
+    o = torch.full_like(qd, 3.0)
+    l = torch.full((B, H, Nq), 3.0, device=DEV)
+    st = _noalloc(qd, kd, kd, S, True, Nk - Nq, 0.088, o, l)
+    torch.cuda.synchronize()
+    assert st == 10
+    assert bool((o == 3.0).all()) and bool((l == 3.0).all()), "a refused call wrote its outputs"
