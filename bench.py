@@ -87,6 +87,28 @@ def load_traffic():
     return t
 
 
+def host_cpu_info() -> dict:
+    """CPU model, physical cores and logical CPUs of this host (lscpu), and the CPUs this
+    process may run on."""
+    import subprocess
+    info = {"logical_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return info
+    fields = {}
+    for line in out.splitlines():
+        if ":" in line:
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    info["model"] = fields.get("Model name")
+    try:
+        info["physical_cores"] = int(fields["Core(s) per socket"]) * int(fields["Socket(s)"])
+    except (KeyError, ValueError):
+        pass
+    return info
+
+
 def cpu_baseline(w, q, k, v, heads: int):
     """Time the fp64 oracle on `heads` heads of batch 0 (all rows)."""
     import numpy as np
@@ -105,8 +127,8 @@ def cpu_baseline(w, q, k, v, heads: int):
     f = metric_flops(1, heads, w.N, w.d, w.causal)
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, all {w.N} rows, fp64 numpy "
-                      f"({dt:.2f} s; BLAS threads = cores)",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+                      f"({dt:.2f} s; cores = the BLAS threads it ran on)",
+            "seconds": dt, "host": host_cpu_info()}
 
 
 def parse_amdsmi_metric(text: str):
@@ -303,6 +325,19 @@ def run(args):
         del src, dst
 
     stream = torch.cuda.current_stream(dev)
+    # Clock settle: untimed launches for about args.settle seconds before the warm-up steps,
+    # so that a short warm-up count (e.g. --warmup 5) does not time the shader clock's ramp
+    # from idle. Reported as settle_launches; the warm-up steps and the timed steps follow
+    # unchanged.
+    settle_launches = 0
+    if args.settle > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.settle:
+            for _ in range(4):
+                step()
+            settle_launches += 4
+            torch.cuda.synchronize()
     if args.warmup is None:
         # Untimed steps until about WARMUP_SECONDS of work has run, so that the shader clock
         # has settled (a short kernel timed from a cold start reads up to 20% slow). The
@@ -427,12 +462,18 @@ def run(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "settle_launches": settle_launches,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(tflops / A100_FIG5D_16K_TFLOPS, 3)
                         if w.name == "long_16k_causal"
                         and not (args.kv_heads or args.bwd or args.fwd_bwd or args.split_kv or args.head_dim)
                         else None),
+        "vs_baseline_basis": ("the pages' FA2 forward figure for this exact workload (causal, d=128, 16k tokens: "
+                              "197 TFLOP/s on A100, Figure 5d); another machine's number, context only"
+                              if w.name == "long_16k_causal"
+                              and not (args.kv_heads or args.bwd or args.fwd_bwd or args.split_kv or args.head_dim)
+                              else None),
         "dtype": "bf16",
         "data": "synthetic",
         "config": config,
@@ -455,7 +496,7 @@ def run(args):
         "gpu_clock": gpu_clock,
     }
     if args.cpu_baseline_heads > 0:
-        out["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_baseline_heads)
+        out["cpu_baseline"] = (cpu_baseline(w, q, k, v, min(args.cpu_baseline_heads, w.H))
                                if not (w.varlen or args.kv_heads or args.bwd or args.fwd_bwd or args.split_kv
                                        or args.head_dim)
                                else None)
@@ -518,8 +559,11 @@ def main():
                     help="override the workload's head dimension (64, 128 or 256)")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped-query attention: K/V with this many heads (must divide H; 0: H)")
-    ap.add_argument("--cpu-baseline-heads", type=int, default=8,
-                    help="(batch, head) pairs of the workload the CPU oracle is timed on (0: skip)")
+    ap.add_argument("--cpu-baseline-heads", type=int, default=16,
+                    help="(batch, head) pairs of batch 0 the CPU oracle is timed on, all rows (0: skip; "
+                         "16 = every head of the long-context workload, about 30 s on a 16-core host)")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="untimed seconds of launches before the warm-up steps (clock settle; 0: none)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB copy kernel (counter calibration for --ingest-counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
