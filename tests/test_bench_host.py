@@ -94,3 +94,22 @@ def test_bwd_and_fwd_bwd_are_exclusive():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--bwd", "--fwd-bwd"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "exclusive" in r.stderr
+
+
+def test_host_cpu_info_fields():
+    info = bench.host_cpu_info()
+    assert info["logical_cpus"] == os.cpu_count()
+    assert 1 <= info["affinity_cpus"] <= info["logical_cpus"]
+    if "physical_cores" in info:
+        assert 1 <= info["physical_cores"] <= info["logical_cpus"]
+
+
+def test_stored_traffic_matches_the_current_kernel_source():
+    """The committed HBM-traffic profile is keyed to the kernel source it was measured on; the
+    bench line reports it only while that source is unchanged."""
+    t = bench.load_traffic()
+    if t is None:
+        pytest.skip("profiles/fa2_fwd_long16k_traffic.json was measured on another kernel source "
+                    "(the bench line then reports traffic: null)")
+    total = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+    assert total >= bench.algorithmic_bytes(WORKLOADS["long_16k_causal"])
