@@ -179,7 +179,10 @@ int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float*
  *   launches nothing. With one piece (num_splits == 1, or N_k == 0) it is fa2_fwd_chunk and
  *   the scratch is not used.
  *   The first call on a device looks up that device's copy of the array (hipGetSymbolAddress,
- *   with the device current); FA2_ERR_NO_DEVICE if that fails.
+ *   with the device current) and keeps the address for the life of the process;
+ *   FA2_ERR_NO_DEVICE if that fails. A device reset (hipDeviceReset) unloads the array, so the
+ *   kept address is not valid afterwards: do not call this entry point on a device after
+ *   resetting it in the same process.
  *   Every call on one device shares that device's scratch, which keeps the last call's
  *   partials (every partial row read by the merge is written by the same call first, so
  *   nothing needs clearing). Calls that overlap on one device (two streams, or two host
