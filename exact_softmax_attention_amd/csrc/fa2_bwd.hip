@@ -165,7 +165,9 @@ struct DqTile {
   static_assert(BC % 32 == 0 && DMA_PER_WAVE >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
 };
 
-template <int D, int BC, bool CAUSAL, bool VARLEN, int NW, int OCC>
+// LA: the K and V row fragments of S^T and dP^T are read LA fragments ahead of the MFMAs
+// that use them (0: the compiler's order, which issues each read one MFMA before its use).
+template <int D, int BC, bool CAUSAL, bool VARLEN, int NW, int OCC, int LA_>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_bwd_dq_kernel(BwdParams p) {
   using TL = DqTile<D, BC, NW>;
@@ -281,13 +283,29 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     for (int kb = 0; kb < TL::NKB; ++kb) {
       s[kb] = (f32x16){};
       dp[kb] = (f32x16){};
+    }
+    {
+      // Fragment f = kb*NKC + kc: its K and V rows are read LA fragments ahead of the two
+      // MFMAs that use them (a ring of LA register pairs; the fences keep the order).
+      constexpr int NF = TL::NKB * TL::NKC;
+      constexpr int LA = LA_ > 0 ? (LA_ < NF ? LA_ : NF) : 1;
+      bf16x8 kr[LA], vr[LA];
+      auto rd = [&](int f) {
+        const int kb = f / TL::NKC, kc = f % TL::NKC;
+        kr[f % LA] = *(const bf16x8*)(stage + kb * 32 * TL::ROWB + roff(kc));
+        vr[f % LA] = *(const bf16x8*)(stage + TL::TILEB + kb * 32 * TL::ROWB + roff(kc));
+      };
 #pragma unroll
-      for (int kc = 0; kc < TL::NKC; ++kc) {
-        const bf16x8 ka = *(const bf16x8*)(stage + kb * 32 * TL::ROWB + roff(kc));
-        const bf16x8 va = *(const bf16x8*)(stage + TL::TILEB + kb * 32 * TL::ROWB + roff(kc));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kc], dp[kb], 0, 0, 0);
+      for (int f = 0; f < LA; ++f) rd(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int kb = f / TL::NKC, kc = f % TL::NKC;
+        if constexpr (LA_ > 0) __builtin_amdgcn_sched_barrier(0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[f % LA], qf[kc], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[f % LA], df[kc], dp[kb], 0, 0, 0);
+        if (f + LA < NF) rd(f + LA);
       }
+      if constexpr (LA_ > 0) __builtin_amdgcn_sched_barrier(0);
     }
     // Causal and ragged masks (key > query, key >= length), as in the forward.
     if ((CAUSAL && key0 + BC - 1 > qw0) || key0 + BC > seq_len) {
@@ -318,18 +336,29 @@ void fa2_bwd_dq_kernel(BwdParams p) {
       dsw[c] = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                        pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
     }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int c = 0; c < TL::NPC; ++c) {
-      const bf16x8 bf = as_bf16x8(dsw[c]);
-#pragma unroll
-      for (int db = 0; db < TL::NDB; ++db) {
+    // dQ^T += K^T dS^T, fragment f = c*NDB + db, its K^T fragment read LA fragments ahead (the
+    // fences let VALU and SALU work cross, not MFMAs or LDS reads).
+    {
+      constexpr int NF = TL::NPC * TL::NDB;
+      constexpr int LA = LA_ > 0 ? (LA_ < NF ? LA_ : NF) : 1;
+      bf16x8 ta[LA];
+      auto rd = [&](int f) {
+        const int c = f / TL::NDB, db = f % TL::NDB;
         const unsigned char* base = stage + 16 * c * TL::ROWB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + toff_lo(db)));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + toff_hi(db)));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf, dqacc[db], 0, 0, 0);
+        ta[f % LA] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+#pragma unroll
+      for (int f = 0; f < LA; ++f) rd(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int c = f / TL::NDB, db = f % TL::NDB;
+        if constexpr (LA_ > 0) __builtin_amdgcn_sched_barrier(0x406);
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[f % LA], as_bf16x8(dsw[c]), dqacc[db], 0, 0, 0);
+        if (f + LA < NF) rd(f + LA);
       }
+      if constexpr (LA_ > 0) __builtin_amdgcn_sched_barrier(0x406);
     }
   };
 
@@ -383,8 +412,9 @@ struct DkvTile {
 };
 
 // KLDS: the wave's K rows are kept in LDS (stored once, in the swizzled layout of the Q row
-// reads) instead of 32 registers, which lets d = 128 run two waves per SIMD.
-template <int D, int BQ, bool CAUSAL, bool VARLEN, int NW, int OCC, bool KLDS>
+// reads) instead of 32 registers, which lets d = 128 run two waves per SIMD. LA as in the dQ
+// kernel, for the Q and dO (and K) row fragments of S and dP.
+template <int D, int BQ, bool CAUSAL, bool VARLEN, int NW, int OCC, bool KLDS, int LA_, int LA_ACC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_bwd_dkdv_kernel(BwdParams p) {
   using TL = DkvTile<D, BQ, NW>;
@@ -518,14 +548,30 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     for (int qb = 0; qb < TL::NQB; ++qb) {
       s[qb] = (f32x16){};
       dp[qb] = (f32x16){};
+    }
+    {
+      // Fragment f = qb*NKC + kc: its Q and dO rows (and the K rows kept in LDS) are read LA
+      // fragments ahead of the two MFMAs that use them.
+      constexpr int NF = TL::NQB * TL::NKC;
+      constexpr int LA = LA_ > 0 ? (LA_ < NF ? LA_ : NF) : 1;
+      bf16x8 qr[LA], dr[LA], kr[LA];
+      auto rd = [&](int f) {
+        const int qb = f / TL::NKC, kc = f % TL::NKC;
+        qr[f % LA] = *(const bf16x8*)(stage + qb * 32 * TL::ROWB + roff(kc));
+        dr[f % LA] = *(const bf16x8*)(stage + TL::TILEB + qb * 32 * TL::ROWB + roff(kc));
+        kr[f % LA] = KLDS ? *(const bf16x8*)(kst + kslab + roff(kc)) : kf[kc];
+      };
 #pragma unroll
-      for (int kc = 0; kc < TL::NKC; ++kc) {
-        const bf16x8 qa = *(const bf16x8*)(stage + qb * 32 * TL::ROWB + roff(kc));
-        const bf16x8 da = *(const bf16x8*)(stage + TL::TILEB + qb * 32 * TL::ROWB + roff(kc));
-        const bf16x8 kk = KLDS ? *(const bf16x8*)(kst + kslab + roff(kc)) : kf[kc];
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kk, s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kc], dp[qb], 0, 0, 0);
+      for (int f = 0; f < LA; ++f) rd(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int qb = f / TL::NKC, kc = f % TL::NKC;
+        if constexpr (LA_ > 0) __builtin_amdgcn_sched_barrier(0);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[f % LA], kr[f % LA], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dr[f % LA], vf[kc], dp[qb], 0, 0, 0);
+        if (f + LA < NF) rd(f + LA);
       }
+      if constexpr (LA_ > 0) __builtin_amdgcn_sched_barrier(0);
     }
     // Masks: query < key (causal), query >= length (ragged tile). With off the entry's query
     // offset minus 4hl (a constant), dead when off < lo or off > hi.
@@ -573,24 +619,34 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
       dsw[c] = (u32x4){pack_bf16x2(de[0], de[1]), pack_bf16x2(de[2], de[3]),
                        pack_bf16x2(de[4], de[5]), pack_bf16x2(de[6], de[7])};
     }
-    // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-    for (int c = 0; c < TL::NPC; ++c) {
-      const bf16x8 pf = as_bf16x8(pw[c]);
-      const bf16x8 sf = as_bf16x8(dsw[c]);
-#pragma unroll
-      for (int db = 0; db < TL::NDB; ++db) {
+    // dV^T += dO^T P, dK^T += Q^T dS, fragment f = c*NDB + db: its dO^T and Q^T fragments
+    // are read LA_ACC fragments ahead (fences as in the dQ kernel).
+    {
+      constexpr int NF = TL::NPC * TL::NDB;
+      constexpr int LA = LA_ACC > 0 ? (LA_ACC < NF ? LA_ACC : NF) : 1;
+      bf16x8 da[LA], qa[LA];
+      auto rd = [&](int f) {
+        const int c = f / TL::NDB, db = f % TL::NDB;
         const unsigned char* qbase = stage + 16 * c * TL::ROWB;
         const unsigned char* dbase = stage + TL::TILEB + 16 * c * TL::ROWB;
         const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + toff_lo(db)));
         const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dbase + toff_hi(db)));
         const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + toff_lo(db)));
         const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, qbase + toff_hi(db)));
-        const bf16x8 da = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 qa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, pf, dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf, dkacc[db], 0, 0, 0);
+        da[f % LA] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        qa[f % LA] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+#pragma unroll
+      for (int f = 0; f < LA; ++f) rd(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int c = f / TL::NDB, db = f % TL::NDB;
+        if constexpr (LA_ACC > 0) __builtin_amdgcn_sched_barrier(0x406);
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[f % LA], as_bf16x8(pw[c]), dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[f % LA], as_bf16x8(dsw[c]), dkacc[db], 0, 0, 0);
+        if (f + LA < NF) rd(f + LA);
       }
+      if constexpr (LA_ACC > 0) __builtin_amdgcn_sched_barrier(0x406);
     }
   };
 
@@ -641,7 +697,8 @@ struct BwdKernels {
   KernelFn dkdv[2][2];
 };
 
-template <int D, int BC_DQ, int NW_DQ, int OCC_DQ, int NW_DKDV, int OCC_DKDV, int BQ_DKDV, bool KLDS>
+template <int D, int BC_DQ, int NW_DQ, int OCC_DQ, int NW_DKDV, int OCC_DKDV, int BQ_DKDV, bool KLDS,
+          int LA_DQ, int LA_DKDV, int LA_DKDV_ACC>
 BwdKernels make_bwd() {
   BwdKernels k;
   k.dq_bc = BC_DQ;
@@ -649,27 +706,28 @@ BwdKernels make_bwd() {
   k.dq_threads = DqTile<D, BC_DQ, NW_DQ>::THREADS;
   k.dkdv_threads = DkvTile<D, BQ_DKDV, NW_DKDV>::THREADS;
   k.dkdv_bk = DkvTile<D, BQ_DKDV, NW_DKDV>::BK;
-  k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false, NW_DQ, OCC_DQ>;
-  k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false, NW_DQ, OCC_DQ>;
-  k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true, NW_DQ, OCC_DQ>;
-  k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true, NW_DQ, OCC_DQ>;
-  k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, false, NW_DKDV, OCC_DKDV, KLDS>;
-  k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, false, NW_DKDV, OCC_DKDV, KLDS>;
-  k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, true, NW_DKDV, OCC_DKDV, KLDS>;
-  k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, true, NW_DKDV, OCC_DKDV, KLDS>;
+  k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false, NW_DQ, OCC_DQ, LA_DQ>;
+  k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false, NW_DQ, OCC_DQ, LA_DQ>;
+  k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true, NW_DQ, OCC_DQ, LA_DQ>;
+  k.dq[1][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, true, NW_DQ, OCC_DQ, LA_DQ>;
+  k.dkdv[0][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, false, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
+  k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, false, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
+  k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, true, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
+  k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, true, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
   return k;
 }
 
 const BwdKernels* bwd_kernels(int d) {
   // <D, dQ key tile, dQ waves, dQ waves per SIMD, dK/dV waves, dK/dV waves per SIMD, dK/dV
-  //  query step, K rows of dK/dV in LDS>: chosen so each kernel keeps as many waves per SIMD
-  //  as its registers allow (d = 128 dK/dV: 32-query steps and K in LDS bring it from one to
-  //  two).
-  static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 4, 3, 32, true>();
-  static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 4, 2, 32, true>();
+  //  query step, K rows of dK/dV in LDS, look-aheads of the dQ S/dP chain, the dK/dV S/dP
+  //  chain and the dK/dV accumulation>: chosen so each kernel keeps as many waves per SIMD as
+  //  its registers allow (d = 128 dK/dV: 32-query steps and K in LDS bring it from one to
+  //  two), then the deepest look-ahead that still fits without spills and measured fastest.
+  static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 4, 3, 32, true, 1, 2, 0>();
+  static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 4, 2, 32, true, 4, 2, 0>();
   // d = 256: the dQ^T, dK^T and dV^T accumulators are 128 registers each, so both kernels run
   // one wave per SIMD (dK/dV: 129 KB of LDS, one workgroup per CU).
-  static const BwdKernels k256 = make_bwd<256, 32, 4, 1, 4, 1, 32, true>();
+  static const BwdKernels k256 = make_bwd<256, 32, 4, 1, 4, 1, 32, true, 4, 4, 2>();
   return d == 64 ? &k64 : d == 128 ? &k128 : d == 256 ? &k256 : nullptr;
 }
 
