@@ -320,22 +320,43 @@ void fa2_fwd_kernel(Params p) {
     // ---- a4: S^T = K_j Q^T ----------------------------------------------------------
     f32x16 s[TL::NKB];
 #pragma unroll
-    for (int kb = 0; kb < TL::NKB; ++kb) {
-      s[kb] = (f32x16){};
+    for (int kb = 0; kb < TL::NKB; ++kb) s[kb] = (f32x16){};
+    if constexpr (TL::NKB == 1 && LA > 0) {
+      // One 32-key chain: scheduling-group hints do not move its K reads ahead, so they are
+      // issued explicitly, SR fragments ahead of their MFMAs, from a ring held in registers
+      // (the fences keep the order).
+      constexpr int SR = LA < TL::NKC ? LA : TL::NKC;
+      bf16x8 kr[SR];
+      auto rd = [&](int kc) {
+        kr[kc % SR] = *(const bf16x8*)(ks + (kc >> 3) * 256 + kaddr[kc & 7]);
+      };
+#pragma unroll
+      for (int kc = 0; kc < SR; ++kc) rd(kc);
 #pragma unroll
       for (int kc = 0; kc < TL::NKC; ++kc) {
-        const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + (kc >> 3) * 256 + kaddr[kc & 7]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kc % SR], qf[kc], s[0], 0, 0, 0);
+        if (kc + SR < TL::NKC) rd(kc + SR);
       }
-    }
-    if constexpr (LA > 0) {
-      // LDS latency: keep LA fragment reads in flight ahead of the MFMA chain.
-      constexpr int NF = TL::NKB * TL::NKC;
-      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int kb = 0; kb < TL::NKB; ++kb) {
+#pragma unroll
+        for (int kc = 0; kc < TL::NKC; ++kc) {
+          const bf16x8 a = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + (kc >> 3) * 256 + kaddr[kc & 7]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+        }
+      }
+      if constexpr (LA > 0) {
+        // LDS latency: keep LA fragment reads in flight ahead of the MFMA chains.
+        constexpr int NF = TL::NKB * TL::NKC;
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     }
 
