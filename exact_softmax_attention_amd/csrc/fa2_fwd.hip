@@ -147,13 +147,16 @@ __device__ __forceinline__ void decode_block(const Params& p, int& bh, int& i) {
 //   kExact:      the pages' recurrence: m = max(m, rowmax) every tile, rescale when it grows.
 //   kLazy:       rowmax every tile, but m only moves when a tile exceeds it by 2^kLazyTau.
 //   kOptimistic: P~ is formed with the current m first; only when a lane's tile sum exceeds
-//                2^kLazyTau (or on the row's first tile) is the true row max taken, the
+//                2^kOptTau (or on the row's first tile) is the true row max taken, the
 //                state rescaled and P~ formed again. m only grows and never passes the
 //                true running max, so no entry underflows earlier than with kExact, and
-//                every P~ entry is at most 2^kLazyTau.
+//                every P~ entry is at most 2^kOptTau. The bound only has to keep the fp32
+//                sums far from overflow (O~ stays below N * 2^kOptTau * max|V|); bf16 and
+//                fp32 rounding are relative, so the size of the entries does not matter.
 enum { kExact = 0, kLazy = 1, kOptimistic = 2 };
 constexpr float kLazyTau = 8.0f;
-constexpr float kOptLimit = 256.0f;   // 2^kLazyTau
+constexpr float kOptTau = 16.0f;
+constexpr float kOptLimit = 65536.0f;   // 2^kOptTau
 
 // LA: how many operand fragments are read from LDS ahead of the MFMA that consumes them
 // (0 leaves the order to the compiler's scheduler). OCC: waves per SIMD the kernel is built
