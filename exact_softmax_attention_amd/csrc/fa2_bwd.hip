@@ -197,32 +197,6 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const int kv_end = CAUSAL ? min(seq_len, q0 + TL::BR) : seq_len;
   const int nt = (kv_end + BC - 1) / BC;
 
-  // This lane's query: Q^T and dO^T as B fragments, L in base 2, and D = rowsum(dO ∘ O)
-  // (each 32-lane half holds 8 of every 16 head-dimension values).
-  const int qw0 = q0 + wave * 32;
-  const int qrow = qw0 + l32;
-  const bool valid = qrow < seq_len;
-  bf16x8 qf[TL::NKC], df[TL::NKC];
-  float dot = 0.f;
-#pragma unroll
-  for (int kc = 0; kc < TL::NKC; ++kc) {
-    u32x4 tq = {0u, 0u, 0u, 0u}, td = tq, to = tq;
-    if (valid && kc * 16 + hl * 8 < dg) {
-      const size_t off = (row0 + (size_t)qrow) * dg + kc * 16 + hl * 8;
-      tq = *(const u32x4*)(p.q + off);
-      td = *(const u32x4*)(p.dout + off);
-      to = *(const u32x4*)(p.o + off);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      dot += bf16_lo(td[e]) * bf16_lo(to[e]) + bf16_hi(td[e]) * bf16_hi(to[e]);
-    qf[kc] = as_bf16x8(tq ^ p.qflip);
-    df[kc] = as_bf16x8(td);
-  }
-  const float drow = halves_sum(dot);
-  const float l2 = valid ? p.lse[row0 + (size_t)qrow] * kLog2e : 0.f;
-  if (valid && hl == 0) p.delta[row0 + (size_t)qrow] = drow;
-
   // K/V staging (direct global -> LDS), both tiles with the dual-pattern swizzle.
   int drow_[TL::DMA_PER_WAVE];
   uint32_t doff[TL::DMA_PER_WAVE];
@@ -249,6 +223,43 @@ void fa2_bwd_dq_kernel(BwdParams p) {
       dma16(vt, doff[d] - back, vs_a + d * 1024);
     }
   };
+
+  dma_tile(0, lds0);
+
+  // This lane's query: Q^T and dO^T as B fragments, L in base 2, and D = rowsum(dO ∘ O)
+  // (each 32-lane half holds 8 of every 16 head-dimension values). Issued after tile 0's
+  // K/V loads and without branches (see col_mask); a row past the end reads row seq_len - 1,
+  // whose values only reach that row's dQ and D, which are never written.
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  const bool valid = qrow < seq_len;
+  const size_t rrow = row0 + (size_t)min(qrow, seq_len - 1);
+  bf16x8 qf[TL::NKC], df[TL::NKC];
+  float dot = 0.f;
+  {
+    u32x4 tq[TL::NKC], td[TL::NKC], to[TL::NKC];
+#pragma unroll
+    for (int kc = 0; kc < TL::NKC; ++kc) {
+      const int col = kc * 16 + hl * 8;
+      const size_t off = rrow * dg + (col < dg ? col : 0);
+      tq[kc] = *(const u32x4*)(p.q + off);
+      td[kc] = *(const u32x4*)(p.dout + off);
+      to[kc] = *(const u32x4*)(p.o + off);
+    }
+#pragma unroll
+    for (int kc = 0; kc < TL::NKC; ++kc) {
+      const uint32_t m = col_mask(kc * 16 + hl * 8, dg);
+      const u32x4 d4 = td[kc] & m, o4 = to[kc] & m;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dot += bf16_lo(d4[e]) * bf16_lo(o4[e]) + bf16_hi(d4[e]) * bf16_hi(o4[e]);
+      qf[kc] = as_bf16x8((tq[kc] & m) ^ p.qflip);
+      df[kc] = as_bf16x8(d4);
+    }
+  }
+  const float drow = halves_sum(dot);
+  const float l2 = p.lse[rrow] * kLog2e;
+  if (valid && hl == 0) p.delta[row0 + (size_t)qrow] = drow;
 
   // Row reads (A operands of S^T and dP^T): row kb*32 + l32, logical chunk 2kc + hl.
   constexpr int NRA = TL::NKC < 8 ? TL::NKC : 8;
@@ -368,8 +379,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  dma_tile(0, lds0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile 0, issued before the row loads
   __syncthreads();
   for (int j = 0; j < nt; j += 2) {
     iteration(j, lds0, lds1);

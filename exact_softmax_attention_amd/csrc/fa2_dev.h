@@ -59,6 +59,17 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// All ones when a row chunk starting at column col lies inside the head dimension dg, else
+// zero: the mask that zeroes padded columns after an unconditional load. The empty asm
+// statement (on the mask, never on loaded data) keeps the optimizer from turning the AND
+// back into a branch around the load, which would make the compiler wait for that load in
+// the middle of a kernel's start-up.
+__device__ __forceinline__ uint32_t col_mask(int col, int dg) {
+  uint32_t m = col < dg ? 0xffffffffu : 0u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+
 // One direct global->LDS load of 4 bytes per lane: lane l's dword at base + voff lands at
 // LDS address lds + 4*l (256 bytes per wave).
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {

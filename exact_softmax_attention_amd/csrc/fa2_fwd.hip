@@ -158,6 +158,27 @@ constexpr float kLazyTau = 8.0f;
 constexpr float kOptTau = 16.0f;
 constexpr float kOptLimit = 65536.0f;   // 2^kOptTau
 
+// A wave's Q^T fragments for its 32 query rows (lane: row qrow, 8 columns per step from
+// 16kc + 8hl), loaded without branches so that every load issues at once: a branch around a
+// load makes the compiler merge the loaded and the default value in a way that waits for
+// that load in the middle of the sequence, one full memory latency at every workgroup's
+// start. A row past the end of the sequence reads row seq_len - 1 instead: its column of S^T
+// concerns no other row, and its O and LSE are never written. Columns past dg (a padded head
+// dimension) are zeroed (col_mask), because K's padded columns repeat real ones.
+template <int NKC>
+__device__ __forceinline__ void load_q_fragments(bf16x8 (&qf)[NKC], const uint16_t* __restrict__ qh, int qrow,
+                                                 int seq_len, int dg, int hl, uint32_t qflip) {
+  const size_t base = (size_t)min(qrow, seq_len - 1) * (size_t)dg;
+  u32x4 t[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const int col = kc * 16 + hl * 8;
+    t[kc] = *(const u32x4*)(qh + base + (col < dg ? col : 0));
+  }
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) qf[kc] = as_bf16x8((t[kc] & col_mask(kc * 16 + hl * 8, dg)) ^ qflip);
+}
+
 // LA: how many operand fragments are read from LDS ahead of the MFMA that consumes them
 // (0 leaves the order to the compiler's scheduler). OCC: waves per SIMD the kernel is built
 // for (its registers are limited to 512 / OCC per lane); more resident waves let one wave's
@@ -229,13 +250,7 @@ void fa2_fwd_kernel(Params p) {
   const int qw0 = q0 + wave * 32;           // first query row of this wave
   const int qrow = qw0 + l32;               // the query this lane's column holds
   bf16x8 qf[TL::NKC];
-#pragma unroll
-  for (int kc = 0; kc < TL::NKC; ++kc) {
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (qrow < seq_len && kc * 16 + hl * 8 < dg) t = *(const u32x4*)(qh + (size_t)qrow * dg + kc * 16 + hl * 8);
-    t ^= p.qflip;
-    qf[kc] = as_bf16x8(t);
-  }
+  load_q_fragments<TL::NKC>(qf, qh, qrow, seq_len, dg, hl, p.qflip);
 
   // ---- a3: K/V staging: global -> LDS directly (1 KB per wave instruction) ------------
   // Instruction b of a tile writes LDS bytes [1024 b, 1024 b + 1024); lane l's 16 bytes land
@@ -622,13 +637,7 @@ void fa2_fwd_kernel_pp(Params p) {
 
   // ---- a2: Q^T fragments ----------------------------------------------------------------
   bf16x8 qf[TL::NKC];
-#pragma unroll
-  for (int kc = 0; kc < TL::NKC; ++kc) {
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (qrow < seq_len && kc * 16 + hl * 8 < dg) t = *(const u32x4*)(qh + (size_t)qrow * dg + kc * 16 + hl * 8);
-    t ^= p.qflip;
-    qf[kc] = as_bf16x8(t);
-  }
+  load_q_fragments<TL::NKC>(qf, qh, qrow, seq_len, dg, hl, p.qflip);
 
   // ---- a3: direct global -> LDS staging into the stage ring -----------------------------
   int drow[TL::DMA_PER_WAVE];
