@@ -432,7 +432,9 @@ def run(args):
     if t is not None:
         traffic = t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
-    variant = fa2.variant_name(w.d, args.variant)
+    # fa2_fwd_varlen picks its own variant; report the one it runs.
+    variant = fa2.variant_name(w.d, fa2.varlen_default_variant(w.d) if (w.varlen and args.variant == 0)
+                               else args.variant)
     config = {"workload": f"{w.name}: {w.description}", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
               "causal": w.causal, "kernel_variant": variant}
     if args.graph:

@@ -25,6 +25,7 @@ from ._lib import (
     lse_merge,
     num_variants,
     variant_name,
+    varlen_default_variant,
 )
 
 
@@ -61,4 +62,5 @@ __all__ = [
     "lse_merge",
     "num_variants",
     "variant_name",
+    "varlen_default_variant",
 ]

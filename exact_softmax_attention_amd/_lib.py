@@ -47,6 +47,7 @@ _SIGNATURES = {
     "fa2_fwd_geometry": ([_c_int] * 6 + [ctypes.POINTER(_c_int)] * 4, _c_int),
     "fa2_status_str": ([_c_int], ctypes.c_char_p),
     "fa2_variant_name": ([_c_int, _c_int], ctypes.c_char_p),
+    "fa2_fwd_varlen_default_variant": ([_c_int], _c_int),
     "fa2_abi_version": ([], _c_int),
 }
 
@@ -95,6 +96,11 @@ def num_variants(d: int) -> int:
 
 def variant_name(d: int, variant: int) -> str:
     return load_library().fa2_variant_name(d, variant).decode()
+
+
+def varlen_default_variant(d: int) -> int:
+    """Index of the variant ``fa2_fwd_varlen`` runs for head dimension d."""
+    return load_library().fa2_fwd_varlen_default_variant(d)
 
 
 def geometry(B: int, H: int, N: int, d: int, causal: bool = False, variant: int = 0) -> dict:

@@ -24,8 +24,10 @@
  *     words (bfloat16 bit patterns). q, k, v, o must be 16-byte aligned; lse 4-byte aligned.
  *   - Ownership: the caller allocates and frees every buffer. The library never allocates,
  *     frees or retains a pointer, and keeps no mutable global state; calls are reentrant.
- *     (The one exception is fa2_fwd_splitkv_noalloc, which keeps its partials in a static
- *     device array of the library; see there.)
+ *     Two exceptions use static device arrays of the library. fa2_fwd_splitkv_noalloc keeps
+ *     its partials in one (see there). The persistent forward variant, which fa2_fwd_varlen
+ *     uses at d = 128, takes its work-queue counters from a pool of sets that every launch
+ *     returns to zero (see fa2_fwd_varlen).
  *   - On success every element of o and lse covered by the call is overwritten (for the
  *     varlen entry: the rows of every sequence, see below). Inputs are never written.
  *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
@@ -36,8 +38,10 @@
  *     launched and nothing is written; the return value says why (FA2_* codes below).
  *   - Problems with zero rows (N == 0, total_tokens == 0 or num_seqs == 0) succeed without a
  *     launch; their pointers may then be NULL.
- *   - Results are deterministic: the forward uses no atomics, so a call with the same
- *     inputs and variant gives bitwise-identical outputs, independent of B and H.
+ *   - Results are deterministic: no arithmetic uses atomics, so a call with the same inputs
+ *     and variant gives bitwise-identical outputs, independent of B and H. (The persistent
+ *     variant's work queue hands out row blocks in a varying order; each block is computed
+ *     the same way whichever workgroup takes it.)
  */
 #ifndef FA2_H_
 #define FA2_H_
@@ -91,6 +95,15 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                tokens covered by no sequence, are then left unwritten.
  *   max_seqlen : upper bound on the sequence lengths (sizes the grid).
  *   causal     : mask within each sequence with sequence-local indices.
+ * At head dimensions that run on the d = 128 kernels (72..128) this call uses the persistent
+ * variant (d128_w8_bc64_persist): one workgroup per CU takes row blocks from a work queue,
+ * so the row blocks past the end of shorter sequences cost no workgroup launch. Its queue
+ * counters live in a static per-device pool of 1024 sets, one set per launch in turn, each
+ * returned to zero by its launch: the pool allocates nothing, and launches in flight at
+ * the same time on one device use different sets as long as fewer than 1024 of them run
+ * at once. A call made while its stream is being captured into a graph launches the
+ * ordinary one-workgroup-per-row-block kernel instead, which gives the same results.
+ * Other head dimensions use variant 0.
  */
 int fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                    const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
@@ -259,6 +272,9 @@ const char* fa2_status_str(int status);
 
 /* Static name of a kernel variant (e.g. "d128_w8_bc64_opt_la4"), or "" if out of range. */
 const char* fa2_variant_name(int d, int variant);
+
+/* The variant fa2_fwd_varlen runs for head dimension d (0 if d is unsupported). Host only. */
+int fa2_fwd_varlen_default_variant(int d);
 
 /* ABI version of this header; bumped on any incompatible change. */
 int fa2_abi_version(void);

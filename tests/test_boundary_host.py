@@ -72,6 +72,15 @@ def test_variants_listed():
     assert fa2.num_variants(100) == 0
 
 
+def test_varlen_default_variant():
+    # fa2_fwd_varlen runs the persistent d = 128 form at head dims 72..128, variant 0 elsewhere.
+    persist = [fa2.variant_name(128, i) for i in range(fa2.num_variants(128))].index("d128_w8_bc64_persist")
+    for d in (72, 96, 120, 128):
+        assert fa2.varlen_default_variant(d) == persist, d
+    for d in (8, 64, 136, 256, 100, 0, 264):
+        assert fa2.varlen_default_variant(d) == 0, d
+
+
 def test_geometry_matches_worked_example():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "llm_infra_atlas_sizing.json")))
     N, d, H, B = g["N"], g["head_dim"], g["heads"], g["batch"]

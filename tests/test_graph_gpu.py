@@ -5,8 +5,9 @@ memset, no host synchronisation), so a caller may capture it in a graph and repl
 Each test captures one call with fixed device buffers. It then replays the graph several
 times, with the program's own eager work between replays: new inputs copied into the
 captured input buffers and the outputs overwritten with NaN. Every replay must reproduce,
-bit for bit, the eager call on the same inputs. The kernels use no atomics, so equal
-inputs give equal bits.
+bit for bit, the eager call on the same inputs. The kernels use no atomics in their
+arithmetic, so equal inputs give equal bits. (Under capture, fa2_fwd_varlen launches the
+one-workgroup-per-row-block kernel in place of its persistent form.)
 """
 import pytest
 import torch
