@@ -122,8 +122,7 @@ struct Tile {
 // contiguous set of heads so the K/V of a head stay in one XCD's L2. Causal launches visit
 // row blocks heaviest first (largest i has the most key tiles).
 template <bool CAUSAL>
-__device__ __forceinline__ void decode_block(const Params& p, int& bh, int& i) {
-  const int id = blockIdx.x;
+__device__ __forceinline__ void decode_block(const Params& p, int id, int& bh, int& i) {
   if (p.heads_per_xcd > 0) {
     const int x = id & 7, slot = id >> 3, hpx = p.heads_per_xcd;
     int hl;
@@ -180,14 +179,14 @@ __device__ __forceinline__ void load_q_fragments(bf16x8 (&qf)[NKC], const uint16
   for (int kc = 0; kc < NKC; ++kc) qf[kc] = as_bf16x8((t[kc] & col_mask(kc * 16 + hl * 8, dg)) ^ qflip);
 }
 
+// One row block (work item id): the whole forward for BR query rows of one (sequence, head).
 // LA: how many operand fragments are read from LDS ahead of the MFMA that consumes them
-// (0 leaves the order to the compiler's scheduler). OCC: waves per SIMD the kernel is built
-// for (its registers are limited to 512 / OCC per lane); more resident waves let one wave's
-// softmax run while another's MFMAs occupy the matrix core.
-template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW = 4,
-          int OCC = (D == 256 ? 1 : 2)>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
-void fa2_fwd_kernel(Params p) {
+// (0 leaves the order to the compiler's scheduler). RING: the K and V^T fragments of every
+// tile are read from explicit register rings fenced by scheduling barriers. Called once per
+// workgroup the scheduling-group hints already pipeline the 64-key tiles (RING = false);
+// nested in the persistent kernel's loop over blocks they no longer hold (RING = true).
+template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW, bool RING>
+__device__ __forceinline__ void fwd_block(const Params& p, int id) {
   using TL = Tile<D, BC, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
@@ -200,7 +199,7 @@ void fa2_fwd_kernel(Params p) {
 
   // ---- a1: work decode ----------------------------------------------------------------
   int bh, i;
-  decode_block<CAUSAL>(p, bh, i);
+  decode_block<CAUSAL>(p, id, bh, i);
   const int bi = bh / p.H;
   const int h = bh - bi * p.H;
   int seq_len, seq_k;   // query rows and keys of this sequence
@@ -340,7 +339,27 @@ void fa2_fwd_kernel(Params p) {
     f32x16 s[TL::NKB];
 #pragma unroll
     for (int kb = 0; kb < TL::NKB; ++kb) s[kb] = (f32x16){};
-    if constexpr (TL::NKB == 1 && LA > 0) {
+    if constexpr (RING) {
+      // Nested in the loop over blocks the scheduling-group hints do not hold, so the K
+      // fragments are read LA ahead from a register ring (fences keep the order).
+      constexpr int NF = TL::NKB * TL::NKC;
+      constexpr int SR = LA > 0 ? (LA < NF ? LA : NF) : 1;
+      bf16x8 kr[SR];
+      auto rd = [&](int f) {
+        const int kb = f / TL::NKC, kc = f % TL::NKC;
+        kr[f % SR] = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + (kc >> 3) * 256 + kaddr[kc & 7]);
+      };
+#pragma unroll
+      for (int f = 0; f < SR; ++f) rd(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int kb = f / TL::NKC, kc = f % TL::NKC;
+        __builtin_amdgcn_sched_barrier(0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[f % SR], qf[kc], s[kb], 0, 0, 0);
+        if (f + SR < NF) rd(f + SR);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (TL::NKB == 1 && LA > 0) {
       // One 32-key chain: scheduling-group hints do not move its K reads ahead, so they are
       // issued explicitly, SR fragments ahead of their MFMAs, from a ring held in registers
       // (the fences keep the order).
@@ -473,368 +492,8 @@ void fa2_fwd_kernel(Params p) {
     lb_run += rsb;
 
     // ---- a7: O~^T += V_j^T P~^T -----------------------------------------------------
-#pragma unroll
-    for (int c = 0; c < TL::NPC; ++c) {
-      const bf16x8 pf = as_bf16x8(pw[c]);
-#pragma unroll
-      for (int db = 0; db < TL::NDB; ++db) {
-        const unsigned char* va = stage + vaddr[db & 3] + (db >> 2) * 256 + 16 * c * TL::ROWB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va + 8 * TL::ROWB));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
-      }
-    }
-    if constexpr (LA > 0) {
-      constexpr int NF = TL::NPC * TL::NDB;       // V^T fragments per tile
-      constexpr int RPF = 2;                      // transposed LDS reads per fragment
-      __builtin_amdgcn_sched_group_barrier(0x100, LA * RPF, 0);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
-      }
-    }
-  };
-
-  // ---- the key/value loop: one barrier per tile ----------------------------------------
-  // Iteration j begins after a barrier that publishes tile j in its stage and certifies
-  // every wave has finished tile j-1, whose stage now takes tile j+1: its direct loads
-  // start, tile j is computed, the loads are waited for, and the next barrier follows.
-  auto iteration = [&](int j, unsigned char* cur, unsigned char* nxt) {
-    if (j + 1 < nt) dma_tile(j + 1, nxt);
-    compute_tile(j, cur);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-  if (nt > 0) dma_tile(0, lds0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int j = 0; j < nt; j += 2) {
-    iteration(j, lds0, lds1);
-    if (j + 1 < nt) iteration(j + 1, lds1, lds0);
-  }
-
-  // ---- a8: epilogue: O = O~ / l, LSE = (m + log2 l) ln 2 --------------------------------
-  // O divides by the sum of the bf16 weights the PV product used; the LSE takes the fp32 sum.
-  const float l_tot = halves_sum(l_run);
-  const float lb_tot = halves_sum(lb_run);
-  if (qrow < seq_len) {
-    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
-    uint16_t* orow = p.o + (orow0 + (size_t)qrow) * dg;
-#pragma unroll
-    for (int db = 0; db < TL::NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
-                   pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        if (db * 32 + 8 * g + 4 * hl < dg) *(u32x2*)(orow + db * 32 + 8 * g + 4 * hl) = w;
-      }
-    if (hl == 0) {
-      p.lse[orow0 + (size_t)qrow] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    }
-  }
-}
-
-// ---- persistent variant ----------------------------------------------------------------
-// The same row-block computation (fwd_block, a copy of fa2_fwd_kernel's body taking the work
-// item id as an argument), run by as many workgroups as the CUs hold. Each workgroup takes
-// row blocks from a work queue in global memory until none is left, so one block's start
-// follows the previous one's end on the CU without a new workgroup's dispatch and start-up.
-// With the XCD-aware order there is one queue per XCD (workgroup w serves queue w % 8, the XCD
-// the round-robin dispatch places it on, and takes the ids x, x + 8, ... of its XCD's heads);
-// otherwise one queue. The next id is fetched at the start of each block (one lane, a vector
-// atomic) and published to the workgroup by the block's own barriers. The last workgroup to
-// finish resets the counters, so that the next launch finds them at zero.
-template <bool CAUSAL>
-__device__ __forceinline__ void decode_block_id(const Params& p, int id, int& bh, int& i) {
-  if (p.heads_per_xcd > 0) {
-    const int x = id & 7, slot = id >> 3, hpx = p.heads_per_xcd;
-    int hl;
-    if (CAUSAL) {
-      i = p.tr - 1 - slot / hpx;
-      hl = slot - (slot / hpx) * hpx;
-    } else {
-      hl = slot / p.tr;
-      i = slot - hl * p.tr;
-    }
-    bh = x * hpx + hl;
-  } else {
-    const int nbh = p.nb * p.H;
-    i = p.tr - 1 - id / nbh;
-    bh = id - (id / nbh) * nbh;
-  }
-}
-
-template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW>
-__device__ __forceinline__ void fwd_block(const Params& p, int id, unsigned char* lds0, unsigned char* lds1) {
-  using TL = Tile<D, BC, NW>;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int l32 = lane & 31;   // MFMA column (query) / A-row index
-  const int hl = lane >> 5;    // which 32-lane half
-
-  // ---- a1: work decode ----------------------------------------------------------------
-  int bh, i;
-  decode_block_id<CAUSAL>(p, id, bh, i);
-  const int bi = bh / p.H;
-  const int h = bh - bi * p.H;
-  int seq_len, seq_k;   // query rows and keys of this sequence
-  // Grouped/multi-query attention: query head h reads key/value head h / g, so the g query
-  // heads of a group share one K/V plane without copies.
-  const int hk = h / p.g;
-  size_t row0;    // index of this sequence's first token in the Q/O/LSE [.., T, D] arrays
-  size_t kvrow0;  // the same token in the K/V arrays
-  if (VARLEN) {
-    int a = p.cu_seqlens[bi];
-    int e = p.cu_seqlens[bi + 1];
-    a = min(max(a, 0), p.T);
-    e = min(max(e, a), p.T);
-    seq_len = e - a;
-    seq_k = seq_len;
-    row0 = (size_t)h * (size_t)p.T + (size_t)a;
-    kvrow0 = (size_t)hk * (size_t)p.T + (size_t)a;
-  } else {
-    seq_len = p.N;
-    seq_k = p.Nk;
-    row0 = (size_t)bh * (size_t)p.N;
-    kvrow0 = ((size_t)bi * (size_t)p.Hkv + (size_t)hk) * (size_t)p.Nk;
-  }
-  // Split-KV: split s of the launch owns keys [s*split_len, (s+1)*split_len) and writes its
-  // partial O and LSE to part s of the output (rows offset by s*part_rows).
-  const int ks0 = VARLEN ? 0 : (int)blockIdx.y * p.split_len;
-  if (!VARLEN) {
-    seq_k = max(min(p.split_len, seq_k - ks0), 0);
-    kvrow0 += (size_t)ks0;
-  }
-  const int diag = p.diag - ks0;
-  const size_t orow0 = row0 + (VARLEN ? 0 : (size_t)blockIdx.y * (size_t)p.part_rows);
-  const int q0 = i * TL::BR;
-  if (q0 >= seq_len) return;  // uniform over the workgroup (varlen rows past the end)
-
-  const int dg = p.dg;            // row pitch of Q, K, V, O in elements
-  const int growb = 2 * dg;       // ... in bytes
-  const uint16_t* __restrict__ qh = p.q + row0 * dg;
-  const unsigned char* kh = (const unsigned char*)(p.k + kvrow0 * dg);
-  const unsigned char* vh = (const unsigned char*)(p.v + kvrow0 * dg);
-
-  // Key tiles to visit: causal stops after the tile holding the last key this block's last
-  // query may attend (none when the whole key range lies after it).
-  const int kv_end = max(CAUSAL ? min(seq_k, q0 + TL::BR + diag) : seq_k, 0);
-  const int nt = (kv_end + BC - 1) / BC;
-
-  // ---- a2: this wave's 32 query rows as MFMA B fragments (Q^T), once -----------------
-  const int qw0 = q0 + wave * 32;           // first query row of this wave
-  const int qrow = qw0 + l32;               // the query this lane's column holds
-  bf16x8 qf[TL::NKC];
-  load_q_fragments<TL::NKC>(qf, qh, qrow, seq_len, dg, hl, p.qflip);
-
-  // ---- a3: K/V staging: global -> LDS directly (1 KB per wave instruction) ------------
-  // Instruction b of a tile writes LDS bytes [1024 b, 1024 b + 1024); lane l's 16 bytes land
-  // at 1024 b + 16 l, i.e. row r = (1024 b + 16 l) / ROWB, physical chunk pch. The lane
-  // therefore fetches the logical chunk pch ^ swz(r) of global row r.
-  int drow[TL::DMA_PER_WAVE];         // tile row each direct load fills
-  uint32_t koff[TL::DMA_PER_WAVE];    // byte offset inside the tile's global rows (K)
-  uint32_t voff[TL::DMA_PER_WAVE];    // same for V
-#pragma unroll
-  for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
-    const int b = wave * TL::DMA_PER_WAVE + d;
-    const int o = b * 1024 + lane * 16;
-    const int r = o / TL::ROWB;
-    const int pch = (o % TL::ROWB) / 16;
-    drow[d] = r;
-    // Padded columns (logical chunk beyond dg) load a real chunk of the same row: finite, and
-    // multiplied by Q's zero columns (K) or landing in unwritten O columns (V).
-    koff[d] = r * growb + (((pch ^ TL::kswz(r)) % (dg / 8)) * 16);
-    voff[d] = r * growb + (((pch ^ TL::vswz(r)) % (dg / 8)) * 16);
-  }
-
-  auto dma_tile = [&](int j, unsigned char* stage) {
-    const int key0 = j * BC;
-    const unsigned char* kt = kh + (size_t)key0 * growb;
-    const unsigned char* vt = vh + (size_t)key0 * growb;
-    const uint32_t ks_a = lds_addr(stage) + wave * TL::DMA_PER_WAVE * 1024;
-    const uint32_t vs_a = lds_addr(stage + TL::TILEB) + wave * TL::DMA_PER_WAVE * 1024;
-    if (key0 + BC <= seq_k) {
-#pragma unroll
-      for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
-        dma16(kt, koff[d], ks_a + d * 1024);
-        dma16(vt, voff[d], vs_a + d * 1024);
-      }
-    } else {
-      // Ragged last tile: rows past the end re-read the last valid row, so every value in
-      // LDS is finite (its probability is zero after the mask).
-      const int last = seq_k - 1 - key0;
-#pragma unroll
-      for (int d = 0; d < TL::DMA_PER_WAVE; ++d) {
-        const uint32_t back = (uint32_t)(drow[d] - min(drow[d], last)) * growb;
-        dma16(kt, koff[d] - back, ks_a + d * 1024);
-        dma16(vt, voff[d] - back, vs_a + d * 1024);
-      }
-    }
-  };
-
-  // Per-lane LDS read offsets (bytes inside a stage), precomputed once. The swizzles only
-  // permute the low four bits of a row's 16-byte chunk index, so logical chunk c + 16 lies
-  // exactly 256 bytes after chunk c: offsets are kept for the first 16 chunks of a row and
-  // the rest reached through the instructions' immediate offset (at d = 256 this keeps 12
-  // registers fewer; at d <= 128 every offset is within the first 16 chunks anyway).
-  //  K (A operand of S^T): row kb*32 + l32, logical chunk 2*kc + hl.
-  constexpr int NKA = TL::NKC < 8 ? TL::NKC : 8;
-  int kaddr[NKA];
-#pragma unroll
-  for (int kc = 0; kc < NKA; ++kc)
-    kaddr[kc] = l32 * TL::ROWB + (((2 * kc + hl) ^ TL::kswz(l32)) * 16);
-  //  V^T (A operand of O^T) by two transposed 8-byte reads per fragment from row-major V:
-  //  the lane supplies row 16c + 8t + 4hl + (lane%16)/4 and columns 32db + 16((lane/16)%2) +
-  //  4(lane%4) .. +3, and receives keys 16c + 8t + 4hl + 0..3 of column d = 32db + l32.
-  const int vr = 4 * hl + ((lane & 15) >> 2);
-  constexpr int NVA = TL::NDB < 4 ? TL::NDB : 4;
-  int vaddr[NVA];
-#pragma unroll
-  for (int db = 0; db < NVA; ++db) {
-    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    vaddr[db] = TL::TILEB + vr * TL::ROWB + (((col >> 3) ^ TL::vswz(vr)) * 16) + (col & 7) * 2;
-  }
-
-  // ---- running state (fp32, registers) -----------------------------------------------
-  f32x16 oacc[TL::NDB];
-#pragma unroll
-  for (int db = 0; db < TL::NDB; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY;  // reference max of S·c (base-2 domain) for this lane's query
-  float l_run = 0.f;        // this lane's partial sum of P~ in fp32 (its half of the keys): LSE
-  float lb_run = 0.f;       // the same sum over P~ as rounded to bf16 for the MFMA: O's divisor
-
-  auto compute_tile = [&](int j, const unsigned char* stage) {
-    const int key0 = j * BC;
-    // a5: a wave whose rows all precede this tile's first key, or whose rows are all past
-    // the end of the sequence, has nothing to add here.
-    if ((CAUSAL && key0 > qw0 + 31 + diag) || qw0 >= seq_len) return;
-    const unsigned char* ks = stage;
-
-    // ---- a4: S^T = K_j Q^T ----------------------------------------------------------
-    f32x16 s[TL::NKB];
-#pragma unroll
-    for (int kb = 0; kb < TL::NKB; ++kb) s[kb] = (f32x16){};
-    {
-      // Nested in the loop over blocks the scheduling-group hints do not hold, so the K
-      // fragments are read LA ahead from a register ring (fences keep the order).
-      constexpr int NF = TL::NKB * TL::NKC;
-      constexpr int SR = LA > 0 ? (LA < NF ? LA : NF) : 1;
-      bf16x8 kr[SR];
-      auto rd = [&](int f) {
-        const int kb = f / TL::NKC, kc = f % TL::NKC;
-        kr[f % SR] = *(const bf16x8*)(ks + kb * 32 * TL::ROWB + (kc >> 3) * 256 + kaddr[kc & 7]);
-      };
-#pragma unroll
-      for (int f = 0; f < SR; ++f) rd(f);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int kb = f / TL::NKC, kc = f % TL::NKC;
-        __builtin_amdgcn_sched_barrier(0);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[f % SR], qf[kc], s[kb], 0, 0, 0);
-        if (f + SR < NF) rd(f + SR);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---- a5: mask on diagonal and ragged tiles only -----------------------------------
-    // Entry (kb, r) of this lane is key key0 + koffs with koffs = kb*32 + 8*(r/4) + 4*hl + r%4.
-    // It is dead when koffs - 4*hl exceeds thr (causal: key > query; ragged: key >= length),
-    // a per-lane threshold; the sign of thr - const selects -inf with one bitfield insert.
-    if ((CAUSAL && key0 + BC - 1 > qw0 + diag) || key0 + BC > seq_k) {
-      int thr = seq_k - 1 - key0 - 4 * hl;
-      if (CAUSAL) thr = min(thr, qrow + diag - key0 - 4 * hl);
-#pragma unroll
-      for (int kb = 0; kb < TL::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kc = kb * 32 + 8 * (r >> 2) + (r & 3);
-          const uint32_t dead = (uint32_t)((thr - kc) >> 31);          // all ones if kc > thr
-          const uint32_t bits = __float_as_uint(s[kb][r]);
-          s[kb][r] = __uint_as_float((bits & ~dead) | (0xff800000u & dead));   // -inf
-        }
-    }
-
-    // ---- a6: online softmax (fp32) --------------------------------------------------
-    // pw[c] holds P~ for PV contraction step c as 4 packed bf16 pairs. Two row sums are
-    // kept: the fp32 sum of P~ (for the LSE) and the sum of P~ as rounded to bf16, i.e.
-    // of exactly the weights the PV product consumes, so that O = O~ / l is a normalised
-    // average of V rows even where one key dominates a row.
-    u32x4 pw[TL::NPC];
-    float rsb;   // the bf16-rounded sum of the last form_p
-    auto form_p = [&](float m_ref) {
-      float rsum = 0.f;
-      rsb = 0.f;
-#pragma unroll
-      for (int c = 0; c < TL::NPC; ++c) {
-        const int kb = c >> 1, r0 = (c & 1) * 8;
-        float e[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          e[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + u], p.c, -m_ref));
-          rsum += e[u];
-        }
-        pw[c] = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                        pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) rsb = sum_bf16x2(pw[c][w], rsb);
-      }
-      return rsum;
-    };
-    auto tile_max = [&]() {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < TL::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      return halves_max(mx) * p.c;   // -inf stays -inf (c > 0)
-    };
-    // Move the reference max to m_new (per lane), rescaling l and O~ by 2^(m_run - m_new).
-    auto rescale_to = [&](float m_new) {
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);   // 0 when m_run = -inf
-      l_run *= alpha;
-      lb_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    };
-    float rs;
-    if (MODE == kOptimistic) {
-      rs = form_p(m_run == -INFINITY ? 0.f : m_run);
-      // Slow path: the row's first tile, or a tile whose P~ grew too large (rs may be inf).
-      if (__builtin_amdgcn_ballot_w64(!(rs <= kOptLimit) || m_run == -INFINITY)) {
-        rescale_to(fmaxf(m_run, tile_max()));
-        rs = form_p(m_run == -INFINITY ? 0.f : m_run);
-      }
-    } else if (MODE == kLazy) {
-      const float mt = tile_max();
-      const bool need = mt > m_run + kLazyTau;    // false when the tile is fully masked
-      if (__builtin_amdgcn_ballot_w64(need)) rescale_to(need ? mt : m_run);
-      rs = form_p(m_run == -INFINITY ? 0.f : m_run);
-    } else {
-      const float m_new = fmaxf(m_run, tile_max());
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-      const bool grew = m_new > m_run;
-      l_run *= alpha;
-      lb_run *= alpha;
-      // Skip the O~ rescale when no row of the wave changed its max (alpha == 1 exactly).
-      if (__builtin_amdgcn_ballot_w64(grew)) {
-#pragma unroll
-        for (int db = 0; db < TL::NDB; ++db) oacc[db] *= alpha;
-      }
-      m_run = m_new;
-      rs = form_p(m_ref);
-    }
-    l_run += rs;
-    lb_run += rsb;
-
-    // ---- a7: O~^T += V_j^T P~^T (V^T fragments read LA ahead from a register ring) -------
-    {
+    if constexpr (RING) {
+      // V^T fragments read LA ahead from a register ring.
       constexpr int NF = TL::NPC * TL::NDB;
       constexpr int VR = LA > 0 ? (LA < NF ? LA : NF) : 1;
       bf16x8 vq[VR];
@@ -855,6 +514,29 @@ __device__ __forceinline__ void fwd_block(const Params& p, int id, unsigned char
         if (f + VR < NF) rdv(f + VR);
       }
       __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < TL::NPC; ++c) {
+        const bf16x8 pf = as_bf16x8(pw[c]);
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db) {
+          const unsigned char* va = stage + vaddr[db & 3] + (db >> 2) * 256 + 16 * c * TL::ROWB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, va + 8 * TL::ROWB));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[db], 0, 0, 0);
+        }
+      }
+      if constexpr (LA > 0) {
+        constexpr int NF = TL::NPC * TL::NDB;       // V^T fragments per tile
+        constexpr int RPF = 2;                      // transposed LDS reads per fragment
+        __builtin_amdgcn_sched_group_barrier(0x100, LA * RPF, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (f + LA < NF) __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
+        }
+      }
     }
   };
 
@@ -898,13 +580,30 @@ __device__ __forceinline__ void fwd_block(const Params& p, int id, unsigned char
   }
 }
 
+// One workgroup per row block. OCC: waves per SIMD the kernel is built for (its registers
+// are limited to 512 / OCC per lane); more resident waves let one wave's softmax run while
+// another's MFMAs occupy the matrix core.
+template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW = 4,
+          int OCC = (D == 256 ? 1 : 2)>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
+void fa2_fwd_kernel(Params p) {
+  fwd_block<D, BC, CAUSAL, VARLEN, MODE, LA, NW, false>(p, (int)blockIdx.x);
+}
+
+// ---- persistent variant ----------------------------------------------------------------
+// The same row-block computation (fwd_block, with its fragment reads in register rings), run
+// by as many workgroups as the CUs hold. Each workgroup takes
+// row blocks from a work queue in global memory until none is left, so one block's start
+// follows the previous one's end on the CU without a new workgroup's dispatch and start-up.
+// With the XCD-aware order there is one queue per XCD (workgroup w serves queue w % 8, the XCD
+// the round-robin dispatch places it on, and takes the ids x, x + 8, ... of its XCD's heads);
+// otherwise one queue. Lane 0 fetches the next id (a vector atomic) while the current block
+// runs and leaves it in LDS, read by all after the block's closing barrier. The last workgroup to
+// finish resets the counters, so that the next launch finds them at zero.
 template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW = 4,
           int OCC = (D == 256 ? 1 : 2)>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_fwd_kernel_persist(Params p, unsigned int* ctr, int total) {
-  using TL = Tile<D, BC, NW>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
   __shared__ int next_id[2];
   const int nq = p.heads_per_xcd > 0 ? 8 : 1;        // queues
   const int q = (int)blockIdx.x % nq;                 // this workgroup's queue
@@ -914,7 +613,7 @@ void fa2_fwd_kernel_persist(Params p, unsigned int* ctr, int total) {
   int id = next_id[0], par = 0;
   while (id < total) {
     if (threadIdx.x == 0) next_id[par ^ 1] = fetch();
-    fwd_block<D, BC, CAUSAL, VARLEN, MODE, LA, NW>(p, id, lds0, lds1);
+    fwd_block<D, BC, CAUSAL, VARLEN, MODE, LA, NW, true>(p, id);
     __syncthreads();
     par ^= 1;
     id = next_id[par];
@@ -979,7 +678,7 @@ void fa2_fwd_kernel_pp(Params p) {
 
   // ---- a1: work decode ----------------------------------------------------------------
   int bh, i;
-  decode_block<CAUSAL>(p, bh, i);
+  decode_block<CAUSAL>(p, (int)blockIdx.x, bh, i);
   const int bi = bh / p.H;
   const int h = bh - bi * p.H;
   int seq_len, seq_k;
