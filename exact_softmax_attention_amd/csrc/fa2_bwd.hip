@@ -92,13 +92,12 @@ __device__ __forceinline__ int dswz(int row) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Workgroup id -> (pair index in [0, npairs), block index). As in the forward: workgroup id
+// Work item id -> (pair index in [0, npairs), block index). As in the forward: workgroup id
 // goes to XCD id % 8 and, when npairs % 8 == 0, each XCD owns a contiguous set of pairs.
 // Causal launches start with the heaviest blocks: HEAVY_HIGH puts the largest block index
 // first (query blocks of the dQ kernel), otherwise the smallest (key blocks of dK/dV).
 template <bool CAUSAL, bool HEAVY_HIGH>
-__device__ __forceinline__ void decode_bwd(int npairs, int nblk, int hpx, int& pair, int& blk) {
-  const int id = blockIdx.x;
+__device__ __forceinline__ void decode_bwd(int id, int npairs, int nblk, int hpx, int& pair, int& blk) {
   if (hpx > 0) {
     const int x = id & 7, slot = id >> 3;
     int hl;
@@ -167,21 +166,24 @@ struct DqTile {
 
 // LA: the K and V row fragments of S^T and dP^T are read LA fragments ahead of the MFMAs
 // that use them (0: the compiler's order, which issues each read one MFMA before its use).
-template <int D, int BC, bool CAUSAL, bool VARLEN, int NW, int OCC, int LA_>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
-void fa2_bwd_dq_kernel(BwdParams p) {
+template <int D, int BC, bool CAUSAL, bool VARLEN, int NW, int LA_, bool PERSIST>
+__device__ __forceinline__ void bwd_dq_block(const BwdParams& p, int id) {
   using TL = DqTile<D, BC, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  // In the persistent kernels this block is one iteration of a loop over blocks. An opaque
+  // copy of the thread id keeps the compiler from hoisting the lane-derived offsets out of
+  // that loop, where they would stay live, and spill, across every block.
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
   int bh, i;
-  decode_bwd<CAUSAL, true>(p.nb * p.H, p.nblk, p.heads_per_xcd, bh, i);
+  decode_bwd<CAUSAL, true>(id, p.nb * p.H, p.nblk, p.heads_per_xcd, bh, i);
   const int bi = bh / p.H;
   const int h = bh - bi * p.H;
   int tok0, seq_len;
@@ -399,6 +401,19 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   }
 }
 
+// One workgroup per 128-row block; or, in the persistent form that varlen calls take at
+// d = 128 and 256, as many workgroups as the CUs hold, taking blocks from a work queue.
+template <int D, int BC, bool CAUSAL, bool VARLEN, int NW, int OCC, int LA_>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
+void fa2_bwd_dq_kernel(BwdParams p) {
+  bwd_dq_block<D, BC, CAUSAL, VARLEN, NW, LA_, false>(p, (int)blockIdx.x);
+}
+template <int D, int BC, bool CAUSAL, bool VARLEN, int NW, int OCC, int LA_>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
+void fa2_bwd_dq_kernel_persist(BwdParams p, unsigned int* ctr, int total) {
+  run_work_queue(ctr, 1, total, [&](int id) { bwd_dq_block<D, BC, CAUSAL, VARLEN, NW, LA_, true>(p, id); });
+}
+
 // ---- dK/dV kernel ----------------------------------------------------------------------
 
 template <int D, int BQ, int NW = 4>
@@ -424,22 +439,25 @@ struct DkvTile {
 // KLDS: the wave's K rows are kept in LDS (stored once, in the swizzled layout of the Q row
 // reads) instead of 32 registers, which lets d = 128 run two waves per SIMD. LA as in the dQ
 // kernel, for the Q and dO (and K) row fragments of S and dP.
-template <int D, int BQ, bool CAUSAL, bool VARLEN, int NW, int OCC, bool KLDS, int LA_, int LA_ACC>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
-void fa2_bwd_dkdv_kernel(BwdParams p) {
+template <int D, int BQ, bool CAUSAL, bool VARLEN, int NW, bool KLDS, int LA_, int LA_ACC, bool PERSIST>
+__device__ __forceinline__ void bwd_dkdv_block(const BwdParams& p, int id) {
   using TL = DkvTile<D, BQ, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char kst[KLDS ? TL::BK * TL::ROWB : 16];
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  // In the persistent kernels this block is one iteration of a loop over blocks. An opaque
+  // copy of the thread id keeps the compiler from hoisting the lane-derived offsets out of
+  // that loop, where they would stay live, and spill, across every block.
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
   int bk, jb;
-  decode_bwd<CAUSAL, false>(p.nb * p.Hkv, p.nblk, p.heads_per_xcd, bk, jb);
+  decode_bwd<CAUSAL, false>(id, p.nb * p.Hkv, p.nblk, p.heads_per_xcd, bk, jb);
   const int bi = bk / p.Hkv;
   const int hk = bk - bi * p.Hkv;
   int tok0, seq_len;
@@ -693,6 +711,18 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+template <int D, int BQ, bool CAUSAL, bool VARLEN, int NW, int OCC, bool KLDS, int LA_, int LA_ACC>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
+void fa2_bwd_dkdv_kernel(BwdParams p) {
+  bwd_dkdv_block<D, BQ, CAUSAL, VARLEN, NW, KLDS, LA_, LA_ACC, false>(p, (int)blockIdx.x);
+}
+template <int D, int BQ, bool CAUSAL, bool VARLEN, int NW, int OCC, bool KLDS, int LA_, int LA_ACC>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
+void fa2_bwd_dkdv_kernel_persist(BwdParams p, unsigned int* ctr, int total) {
+  run_work_queue(ctr, 1, total,
+                 [&](int id) { bwd_dkdv_block<D, BQ, CAUSAL, VARLEN, NW, KLDS, LA_, LA_ACC, true>(p, id); });
+}
+
 // ---- host side ------------------------------------------------------------------------
 
 typedef const void* KernelFn;
@@ -705,10 +735,16 @@ struct BwdKernels {
   int dkdv_bk;           // keys per dK/dV workgroup
   KernelFn dq[2][2];     // [varlen][causal]
   KernelFn dkdv[2][2];
+  // Persistent forms, taken by varlen calls outside graph capture: workgroups per CU (0: none)
+  // and the kernels, [causal].
+  int dq_wg_per_cu = 0;
+  int dkdv_wg_per_cu = 0;
+  KernelFn dq_persist[2] = {nullptr, nullptr};
+  KernelFn dkdv_persist[2] = {nullptr, nullptr};
 };
 
 template <int D, int BC_DQ, int NW_DQ, int OCC_DQ, int NW_DKDV, int OCC_DKDV, int BQ_DKDV, bool KLDS,
-          int LA_DQ, int LA_DKDV, int LA_DKDV_ACC>
+          int LA_DQ, int LA_DKDV, int LA_DKDV_ACC, bool PERSIST_DQ, bool PERSIST_DKDV>
 BwdKernels make_bwd() {
   BwdKernels k;
   k.dq_bc = BC_DQ;
@@ -724,20 +760,35 @@ BwdKernels make_bwd() {
   k.dkdv[0][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, false, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
   k.dkdv[1][0] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, false, true, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
   k.dkdv[1][1] = (KernelFn)&fa2_bwd_dkdv_kernel<D, BQ_DKDV, true, true, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
+  if constexpr (PERSIST_DQ) {
+    k.dq_wg_per_cu = 4 * OCC_DQ / NW_DQ;
+    k.dq_persist[0] = (KernelFn)&fa2_bwd_dq_kernel_persist<D, BC_DQ, false, true, NW_DQ, OCC_DQ, LA_DQ>;
+    k.dq_persist[1] = (KernelFn)&fa2_bwd_dq_kernel_persist<D, BC_DQ, true, true, NW_DQ, OCC_DQ, LA_DQ>;
+  }
+  if constexpr (PERSIST_DKDV) {
+    k.dkdv_wg_per_cu = 4 * OCC_DKDV / NW_DKDV;
+    k.dkdv_persist[0] =
+        (KernelFn)&fa2_bwd_dkdv_kernel_persist<D, BQ_DKDV, false, true, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
+    k.dkdv_persist[1] =
+        (KernelFn)&fa2_bwd_dkdv_kernel_persist<D, BQ_DKDV, true, true, NW_DKDV, OCC_DKDV, KLDS, LA_DKDV, LA_DKDV_ACC>;
+  }
   return k;
 }
 
 const BwdKernels* bwd_kernels(int d) {
   // <D, dQ key tile, dQ waves, dQ waves per SIMD, dK/dV waves, dK/dV waves per SIMD, dK/dV
   //  query step, K rows of dK/dV in LDS, look-aheads of the dQ S/dP chain, the dK/dV S/dP
-  //  chain and the dK/dV accumulation>: chosen so each kernel keeps as many waves per SIMD as
-  //  its registers allow (d = 128 dK/dV: 32-query steps and K in LDS bring it from one to
-  //  two), then the deepest look-ahead that still fits without spills and measured fastest.
-  static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 4, 3, 32, true, 1, 2, 0>();
-  static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 4, 2, 32, true, 4, 2, 0>();
+  //  chain and the dK/dV accumulation, persistent dQ and dK/dV forms for varlen calls>:
+  //  chosen so each kernel keeps as many waves per SIMD as its registers allow (d = 128
+  //  dK/dV: 32-query steps and K in LDS bring it from one to two), then the deepest
+  //  look-ahead that still fits without spills and measured fastest. The persistent forms
+  //  pay at d = 128 and 256 (16 packed sequences: +8% and +20%); at d = 64, with three and
+  //  four workgroups per CU, the dQ form measured 4% slower and the dK/dV form no faster.
+  static const BwdKernels k64 = make_bwd<64, 32, 4, 4, 4, 3, 32, true, 1, 2, 0, false, false>();
+  static const BwdKernels k128 = make_bwd<128, 32, 4, 2, 4, 2, 32, true, 4, 2, 0, true, true>();
   // d = 256: the dQ^T, dK^T and dV^T accumulators are 128 registers each, so both kernels run
   // one wave per SIMD (dK/dV: 129 KB of LDS, one workgroup per CU).
-  static const BwdKernels k256 = make_bwd<256, 32, 4, 1, 4, 1, 32, true, 4, 4, 2>();
+  static const BwdKernels k256 = make_bwd<256, 32, 4, 1, 4, 1, 32, true, 4, 4, 2, true, true>();
   return d == 64 ? &k64 : d == 128 ? &k128 : d == 256 ? &k256 : nullptr;
 }
 
@@ -751,26 +802,56 @@ bool aligned_to(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)
 bool bwd_head_dim(int d) { return d >= 8 && d <= 256 && d % 8 == 0; }
 int bwd_padded_dim(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
 
+// One launch of a backward kernel over num_wg work items: one workgroup per item, or, for the
+// persistent form (wg_per_cu > 0), min(num_wg, CUs * wg_per_cu) workgroups sharing a work
+// queue whose counters come from the library's pool.
+int bwd_kernel_launch(KernelFn plain, KernelFn persist, int wg_per_cu, int threads, BwdParams& p,
+                      long long num_wg, int dev, void* stream) {
+  if (persist && wg_per_cu > 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return FA2_ERR_NO_DEVICE;
+    unsigned int* ctr = nullptr;
+    const int st = fa2_internal::queue_counters(dev, &ctr);
+    if (st != FA2_OK) return st;
+    int total = (int)num_wg;
+    const long long grid = num_wg < (long long)cus * wg_per_cu ? num_wg : (long long)cus * wg_per_cu;
+    void* args[] = {&p, &ctr, &total};
+    return hipLaunchKernel(persist, dim3((unsigned)grid), dim3((unsigned)threads), args, 0,
+                           (hipStream_t)stream) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+  }
+  void* args[] = {&p};
+  return hipLaunchKernel(plain, dim3((unsigned)num_wg), dim3((unsigned)threads), args, 0,
+                         (hipStream_t)stream) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
 int bwd_launch(const BwdKernels& kk, bool varlen, bool causal, BwdParams p, int nblk_q, int nblk_k,
                long long npairs_q, long long npairs_k, void* stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FA2_ERR_NO_DEVICE;
   const int v = varlen ? 1 : 0, c = causal ? 1 : 0;
+  // Varlen calls take the persistent forms where they exist: the blocks past the end of the
+  // shorter sequences cost a queue fetch instead of a workgroup launch. Under stream capture a graph would keep
+  // the counter sets it captured, so captured calls take the one-block-per-workgroup kernels
+  // (same blocks, same results).
+  bool persist = varlen;
+  if (persist) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing((hipStream_t)stream, &cap) != hipSuccess) return FA2_ERR_LAUNCH;
+    persist = cap == hipStreamCaptureStatusNone;
+  }
   p.nblk = nblk_q;
   // Per-XCD pair ranges for fixed-length batches; varlen uses the plain heaviest-first order
   // (with unequal sequence lengths the per-XCD ranges get unequal shares, as in the forward).
   p.heads_per_xcd = (!varlen && npairs_q % 8 == 0) ? (int)(npairs_q / 8) : 0;
-  void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(kk.dq[v][c], dim3((unsigned)(nblk_q * npairs_q)),
-                                 dim3((unsigned)kk.dq_threads), args, 0, (hipStream_t)stream);
-  if (e != hipSuccess) return FA2_ERR_LAUNCH;
+  int st = bwd_kernel_launch(kk.dq[v][c], persist ? kk.dq_persist[c] : nullptr, kk.dq_wg_per_cu,
+                             kk.dq_threads, p, nblk_q * npairs_q, dev, stream);
+  if (st != FA2_OK) return st;
   BwdParams p2 = p;
   p2.nblk = nblk_k;
   p2.heads_per_xcd = (!varlen && npairs_k % 8 == 0) ? (int)(npairs_k / 8) : 0;
-  void* args2[] = {&p2};
-  e = hipLaunchKernel(kk.dkdv[v][c], dim3((unsigned)(nblk_k * npairs_k)),
-                      dim3((unsigned)kk.dkdv_threads), args2, 0, (hipStream_t)stream);
-  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+  return bwd_kernel_launch(kk.dkdv[v][c], persist ? kk.dkdv_persist[c] : nullptr, kk.dkdv_wg_per_cu,
+                           kk.dkdv_threads, p2, nblk_k * npairs_k, dev, stream);
 }
 
 int bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -1,7 +1,8 @@
 // fa2_dev.h — device-side helpers shared by the gfx950 attention kernels (forward and
 // backward): vector types, bf16 packing, direct global->LDS loads, LDS addressing and the
-// cross-half reductions of a 64-lane wave. Included by each kernel source; everything here
-// has internal linkage.
+// cross-half reductions of a 64-lane wave, and the work loop of the persistent kernels.
+// Included by each kernel source; everything here has internal linkage except the
+// declaration of the host function that hands out work-queue counters.
 #ifndef FA2_DEV_H_
 #define FA2_DEV_H_
 
@@ -76,6 +77,44 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
   asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
+// Work loop of the persistent kernels. Every workgroup takes work item ids from queue
+// q = blockIdx.x % nq of the counter set ctr (queue q hands out q, q + nq, q + 2 nq, ...) and
+// runs block(id) for each, until the ids reach total. Lane 0 fetches the next id (a vector
+// atomic) while the current block runs and leaves it in LDS, where the workgroup reads it
+// after the barrier that closes the block. ctr[8] counts the workgroups that have finished;
+// the last one returns ctr[0..8] to zero for the next launch that takes the set. block(id)
+// must be uniform over the workgroup in its barriers (an early return is taken by all).
+template <typename Block>
+__device__ __forceinline__ void run_work_queue(unsigned int* ctr, int nq, int total, Block&& block) {
+  __shared__ int next_id[2];
+  const int q = (int)blockIdx.x % nq;
+  auto fetch = [&]() { return (int)atomicAdd(&ctr[q], 1u) * nq + q; };
+  if (threadIdx.x == 0) next_id[0] = fetch();
+  __syncthreads();
+  int id = next_id[0], par = 0;
+  while (id < total) {
+    if (threadIdx.x == 0) next_id[par ^ 1] = fetch();
+    block(id);
+    __syncthreads();
+    par ^= 1;
+    id = next_id[par];
+  }
+  if (threadIdx.x == 0) {
+    __threadfence();
+    if (atomicAdd(&ctr[8], 1u) == gridDim.x - 1) {
+#pragma unroll
+      for (int c = 0; c < 9; ++c) atomicExch(&ctr[c], 0u);
+    }
+  }
+}
+
 }  // namespace
+
+// Host side, defined with the forward: the device address of the next counter set (16 words)
+// of a per-device pool for a persistent launch on device dev; sets are taken in turn and
+// each is zero when taken. Returns a status code.
+namespace fa2_internal {
+int queue_counters(int dev, unsigned int** out);
+}
 
 #endif  // FA2_DEV_H_

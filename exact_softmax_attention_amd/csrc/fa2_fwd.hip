@@ -191,7 +191,11 @@ __device__ __forceinline__ void fwd_block(const Params& p, int id) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGEB];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGEB];
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  // In the persistent kernel this block is one iteration of a loop over blocks. An opaque
+  // copy of the thread id keeps the compiler from hoisting the lane-derived offsets out of
+  // that loop, where they would stay live across every block.
+  if constexpr (RING) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int l32 = lane & 31;   // MFMA column (query) / A-row index
@@ -592,39 +596,18 @@ void fa2_fwd_kernel(Params p) {
 
 // ---- persistent variant ----------------------------------------------------------------
 // The same row-block computation (fwd_block, with its fragment reads in register rings), run
-// by as many workgroups as the CUs hold. Each workgroup takes
-// row blocks from a work queue in global memory until none is left, so one block's start
-// follows the previous one's end on the CU without a new workgroup's dispatch and start-up.
-// With the XCD-aware order there is one queue per XCD (workgroup w serves queue w % 8, the XCD
-// the round-robin dispatch places it on, and takes the ids x, x + 8, ... of its XCD's heads);
-// otherwise one queue. Lane 0 fetches the next id (a vector atomic) while the current block
-// runs and leaves it in LDS, read by all after the block's closing barrier. The last workgroup to
-// finish resets the counters, so that the next launch finds them at zero.
+// by as many workgroups as the CUs hold. Each workgroup takes row blocks from a work queue in
+// global memory (run_work_queue) until none is left, so one block's start follows the
+// previous one's end on the CU without a new workgroup's dispatch and start-up. With the
+// XCD-aware order there is one queue per XCD (workgroup w serves queue w % 8, the XCD the
+// round-robin dispatch places it on, and takes the ids x, x + 8, ... of its XCD's heads);
+// otherwise one queue.
 template <int D, int BC, bool CAUSAL, bool VARLEN, int MODE, int LA, int NW = 4,
           int OCC = (D == 256 ? 1 : 2)>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(OCC, OCC)))
 void fa2_fwd_kernel_persist(Params p, unsigned int* ctr, int total) {
-  __shared__ int next_id[2];
-  const int nq = p.heads_per_xcd > 0 ? 8 : 1;        // queues
-  const int q = (int)blockIdx.x % nq;                 // this workgroup's queue
-  auto fetch = [&]() { return (int)atomicAdd(&ctr[q], 1u) * nq + q; };
-  if (threadIdx.x == 0) next_id[0] = fetch();
-  __syncthreads();
-  int id = next_id[0], par = 0;
-  while (id < total) {
-    if (threadIdx.x == 0) next_id[par ^ 1] = fetch();
-    fwd_block<D, BC, CAUSAL, VARLEN, MODE, LA, NW, true>(p, id);
-    __syncthreads();
-    par ^= 1;
-    id = next_id[par];
-  }
-  if (threadIdx.x == 0) {
-    __threadfence();
-    if (atomicAdd(&ctr[8], 1u) == gridDim.x - 1) {
-#pragma unroll
-      for (int c = 0; c < 9; ++c) atomicExch(&ctr[c], 0u);
-    }
-  }
+  run_work_queue(ctr, p.heads_per_xcd > 0 ? 8 : 1, total,
+                 [&](int id) { fwd_block<D, BC, CAUSAL, VARLEN, MODE, LA, NW, true>(p, id); });
 }
 
 // ---- ping-pong variant ---------------------------------------------------------------
@@ -1117,8 +1100,9 @@ std::mutex persist_mu;
 unsigned int* persist_base[kMaxQueueDevices];   // device address of persist_ctr, per device
 unsigned long long persist_next[kMaxQueueDevices];
 
-// The counter set for the next persistent launch on device dev.
-int next_counter_set(int dev, unsigned int** out) {
+}  // namespace
+
+int fa2_internal::queue_counters(int dev, unsigned int** out) {
   if (dev < 0 || dev >= kMaxQueueDevices) return FA2_ERR_NO_DEVICE;
   std::lock_guard<std::mutex> lock(persist_mu);
   if (!persist_base[dev]) {
@@ -1129,6 +1113,8 @@ int next_counter_set(int dev, unsigned int** out) {
   *out = persist_base[dev] + 16 * (persist_next[dev]++ % kQueueSlots);
   return FA2_OK;
 }
+
+namespace {
 
 int launch(const Variant& var, bool varlen, bool causal, Params& p, int num_wg, void* stream,
            int grid_y = 1) {
@@ -1146,7 +1132,7 @@ int launch(const Variant& var, bool varlen, bool causal, Params& p, int num_wg, 
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return FA2_ERR_NO_DEVICE;
     unsigned int* ctr = nullptr;
-    const int st = next_counter_set(dev, &ctr);
+    const int st = fa2_internal::queue_counters(dev, &ctr);
     if (st != FA2_OK) return st;
     int total = num_wg;
     const int grid = std::min(num_wg, cus * var.wg_per_cu);

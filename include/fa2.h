@@ -25,9 +25,9 @@
  *   - Ownership: the caller allocates and frees every buffer. The library never allocates,
  *     frees or retains a pointer, and keeps no mutable global state; calls are reentrant.
  *     Two exceptions use static device arrays of the library. fa2_fwd_splitkv_noalloc keeps
- *     its partials in one (see there). The persistent forward variant, which fa2_fwd_varlen
- *     uses at d = 128, takes its work-queue counters from a pool of sets that every launch
- *     returns to zero (see fa2_fwd_varlen).
+ *     its partials in one (see there). The persistent kernels, which fa2_fwd_varlen uses at
+ *     d = 72..128 and fa2_bwd_varlen at d = 72..256, take their work-queue counters from a
+ *     pool of sets that every launch returns to zero (see fa2_fwd_varlen).
  *   - On success every element of o and lse covered by the call is overwritten (for the
  *     varlen entry: the rows of every sequence, see below). Inputs are never written.
  *   - stream is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
@@ -40,8 +40,8 @@
  *     launch; their pointers may then be NULL.
  *   - Results are deterministic: no arithmetic uses atomics, so a call with the same inputs
  *     and variant gives bitwise-identical outputs, independent of B and H. (The persistent
- *     variant's work queue hands out row blocks in a varying order; each block is computed
- *     the same way whichever workgroup takes it.)
+ *     kernels' work queues hand out blocks in a varying order; each block is computed the
+ *     same way whichever workgroup takes it.)
  */
 #ifndef FA2_H_
 #define FA2_H_
@@ -241,10 +241,15 @@ int fa2_lse_merge(const void* o_parts, const float* lse_parts, int num_parts, lo
  *   padded as in the forward); causal and scale as for the forward (same scale as the
  *   forward).
  *   dq, dk, dv and delta are fully overwritten on success; they must not alias the inputs.
- * Two kernels run in order on stream (dQ and D, then dK and dV); no atomics are used, so the
- * gradients are bitwise reproducible. Validation, ownership and zero-size rules as fa2_fwd.
+ * Two kernels run in order on stream (dQ and D, then dK and dV); no arithmetic uses atomics,
+ * so the gradients are bitwise reproducible. Validation, ownership and zero-size rules as
+ * fa2_fwd.
  * Varlen: q, o, dout, dq [H, T, d]; k, v, dk, dv [H_kv, T, d]; lse, delta [H, T];
- * cu_seqlens as for fa2_fwd_varlen (tokens covered by no sequence are left unwritten).
+ * cu_seqlens as for fa2_fwd_varlen (tokens covered by no sequence are left unwritten). At
+ * head dimensions 72..256 both kernels run in their persistent forms, which take blocks
+ * from work queues whose counters come from the pool described at fa2_fwd_varlen (two sets
+ * per call); under stream capture the ordinary kernels run instead. Results are the same
+ * bits either way.
  */
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
             const void* dout, void* dq, void* dk, void* dv, float* delta,

@@ -6,8 +6,9 @@ Each test captures one call with fixed device buffers. It then replays the graph
 times, with the program's own eager work between replays: new inputs copied into the
 captured input buffers and the outputs overwritten with NaN. Every replay must reproduce,
 bit for bit, the eager call on the same inputs. The kernels use no atomics in their
-arithmetic, so equal inputs give equal bits. (Under capture, fa2_fwd_varlen launches the
-one-workgroup-per-row-block kernel in place of its persistent form.)
+arithmetic, so equal inputs give equal bits. (Under capture, fa2_fwd_varlen and
+fa2_bwd_varlen launch their one-workgroup-per-block kernels in place of the persistent
+forms.)
 """
 import pytest
 import torch

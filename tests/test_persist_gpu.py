@@ -1,13 +1,16 @@
-"""The persistent forward (a fixed grid of workgroups taking row blocks from a work queue),
-which fa2_fwd_varlen runs at head dimensions 72..128.
+"""The persistent kernels: a fixed grid of workgroups taking blocks from a work queue. The
+forward's runs in fa2_fwd_varlen at head dimensions 72..128; the backward's dQ and dK/dV
+forms run in fa2_bwd_varlen at head dimensions 72..256.
 
-Its tiles are those of the ordinary d = 128 kernel of the same shape (variant 0), so every
-output must match that kernel bit for bit, whichever workgroup takes a row block. The queue
-counters come from a static pool of sets that each launch returns to zero; the tests run
-more launches than the pool has sets (so every set is reused), interleave launches on
-several streams, and prefill the outputs with NaN so that a row block the queue skipped
-shows up. Parity against the oracle runs here as well, on batches with empty, one-token and
-tile-edge sequences.
+Their blocks are those of the ordinary kernels, so every output must match those kernels
+bit for bit, whichever workgroup takes a block. The forward is compared with variant 0
+(the ordinary kernel of the same tiles). The backward is compared with the same call
+captured in a graph, since under capture fa2_bwd_varlen launches the ordinary kernels. The
+queue counters come from a static pool of sets that each launch returns to zero. The tests
+therefore run more launches than the pool has sets, so every set is reused, and interleave
+launches on several streams. Outputs are prefilled with NaN so that a block the queue
+skipped shows up. Parity against the oracle runs here as well, on batches with empty,
+one-token and tile-edge sequences.
 """
 import math
 
@@ -16,7 +19,7 @@ import pytest
 import torch
 
 import exact_softmax_attention_amd as fa2
-from oracle import attention_varlen
+from oracle import attention_backward_varlen, attention_varlen
 from synthetic import make_qkv, make_varlen
 
 pytestmark = pytest.mark.gpu
@@ -139,3 +142,94 @@ def test_fixed_length_persistent_variant(causal):
         torch.cuda.synchronize()
         for a, b in zip(s0, s1):
             assert torch.equal(a, b), (splits, diag)
+
+
+def _bwd_varlen_case(H, d, seed, lengths, causal):
+    (q, k, v, cu, lengths), (qd, kd, vd, cud) = _varlen_on_device(H, d, seed, lengths)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa2.fwd_varlen(qd, kd, vd, cud, max(lengths), causal=causal, scale=scale)
+    gen = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn(q.shape, generator=gen).to(torch.bfloat16)
+    return (q, k, v, cu, lengths, dout), (qd, kd, vd, o, lse, dout.to(DEV), cud), scale
+
+
+def _nan_grads(qd, kd, vd, lse):
+    return (torch.full_like(qd, float("nan")), torch.full_like(kd, float("nan")),
+            torch.full_like(vd, float("nan")), torch.full_like(lse, float("nan")))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_varlen_persistent_matches_ordinary(d, causal):
+    """Eager fa2_bwd_varlen (persistent kernels) against the same call captured in a graph
+    (ordinary kernels): bitwise equal; and against the oracle's backward."""
+    lengths = [0, 1, 2, 127, 128, 129, 0, 700, 5, 1000, 64, 1]
+    host, dev, scale = _bwd_varlen_case(2, d, 1350 + d + int(causal), lengths, causal)
+    qd, kd, vd, o, lse, dout, cud = dev
+    maxlen = max(host[4])
+    dq, dk, dv, delta = _nan_grads(qd, kd, vd, lse)
+    print(f"[case] persistent bwd varlen d{d} causal={causal}", flush=True)
+    fa2.bwd_varlen(qd, kd, vd, o, lse, dout, cud, maxlen, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv,
+                   delta=delta)
+    torch.cuda.synchronize()
+    cq, ck, cv, cdelta = _nan_grads(qd, kd, vd, lse)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        fa2.bwd_varlen(qd, kd, vd, o, lse, dout, cud, maxlen, causal=causal, scale=scale, dq=cq, dk=ck, dv=cv,
+                       delta=cdelta)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for t in (cq, ck, cv, cdelta):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b, name in ((dq, cq, "dq"), (dk, ck, "dk"), (dv, cv, "dv"), (delta, cdelta, "delta")):
+            assert torch.equal(a, b), f"{name} of the persistent kernels differs from the ordinary ones (replay {rep})"
+    q, k, v, cu, lengths, dout_h = host
+    ref = attention_backward_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                    dout_h.double().numpy(), cu.numpy(), causal, scale)
+    # Gradient tolerance as in the backward parity tests: relative to the largest reference
+    # entry, max 2e-2 and mean 2e-3 (a few bf16 roundings of the summed terms).
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        err = np.abs(got.float().cpu().double().numpy() - want)
+        top = float(np.abs(want).max())
+        print(f"[parity] persistent bwd d{d} causal={causal} {name}: max {err.max() / top:.2e} "
+              f"mean {err.mean() / top:.2e} of max|ref| {top:.3e}", flush=True)
+        assert np.all(np.isfinite(err)) and err.max() <= 2e-2 * top and err.mean() <= 2e-3 * top
+
+
+def test_bwd_pool_reuse_and_streams():
+    """Backward varlen calls (two counter sets each) past the pool's size, then on three
+    streams at once: every result equals the first call's."""
+    cases = []
+    for j, lengths in enumerate(([900, 3, 0, 1500], [64] * 12, [1, 2000])):
+        host, dev, scale = _bwd_varlen_case(2, 128, 1370 + j, lengths, causal=bool(j % 2))
+        qd, kd, vd, o, lse, dout, cud = dev
+        ref = fa2.bwd_varlen(qd, kd, vd, o, lse, dout, cud, max(host[4]), causal=bool(j % 2), scale=scale)
+        cases.append((max(host[4]), dev, scale, bool(j % 2), [r.clone() for r in ref]))
+    torch.cuda.synchronize()
+    calls = POOL_SETS // 2 + 40
+    for i in range(calls):
+        maxlen, (qd, kd, vd, o, lse, dout, cud), scale, causal, ref = cases[i % 2]
+        out = fa2.bwd_varlen(qd, kd, vd, o, lse, dout, cud, maxlen, causal=causal, scale=scale)
+        if i % 50 == 0 or i >= calls - 2:
+            torch.cuda.synchronize()
+            for a, b in zip(out, ref):
+                assert torch.equal(a, b), f"call {i}"
+        if i % 200 == 0:
+            print(f"[case] bwd pool reuse call {i} of {calls}", flush=True)
+    streams = [torch.cuda.Stream() for _ in cases]     # default priority
+    for rep in range(3):
+        print(f"[case] bwd three streams rep {rep}", flush=True)
+        outs = []
+        for (maxlen, (qd, kd, vd, o, lse, dout, cud), scale, causal, _), st in zip(cases, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                outs.append(fa2.bwd_varlen(qd, kd, vd, o, lse, dout, cud, maxlen, causal=causal, scale=scale))
+        torch.cuda.synchronize()
+        for out, case in zip(outs, cases):
+            for a, b in zip(out, case[4]):
+                assert torch.equal(a, b)
