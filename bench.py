@@ -69,11 +69,12 @@ def algorithmic_bytes(w, lengths=None, kv_heads=None) -> int:
     return 4 * w.B * (w.H + hk) * w.N * w.d + 4 * w.B * w.H * w.N
 
 
-def bwd_algorithmic_bytes(w, kv_heads=None) -> int:
+def bwd_algorithmic_bytes(w, kv_heads=None, lengths=None) -> int:
     """Backward: read Q, K, V, O, dO and LSE once, write dQ, dK, dV once (bf16); D is
     written and read once (fp32)."""
     hk = w.H if kv_heads is None else kv_heads
-    rows_q, rows_kv = w.B * w.H * w.N, w.B * hk * w.N
+    tokens = sum(lengths) if w.varlen else w.B * w.N
+    rows_q, rows_kv = w.H * tokens, hk * tokens
     return 2 * w.d * (4 * rows_q + 4 * rows_kv) + 4 * rows_q + 8 * rows_q
 
 
@@ -288,28 +289,34 @@ def run(args):
                       "fns": (one_pass, merge_only)}
 
     if args.bwd or args.fwd_bwd:
-        if w.varlen:
-            raise SystemExit("--bwd / --fwd-bwd run on fixed-length workloads")
         gen = torch.Generator(device="cpu").manual_seed(1000 + w.seed)
         dod = torch.randn(qd.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).to(dev)
-        if kd.shape[1] == qd.shape[1]:
-            fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if w.varlen:
+            fwd_step = lambda: fa2.fwd_varlen(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o,
+                                              lse=lse, variant=entry_variant)
+        elif kd.shape[1] == qd.shape[1]:
+            fwd_step = lambda: fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                                       variant=entry_variant)
         else:
-            fa2.fwd_gqa(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            fwd_step = lambda: fa2.fwd_gqa(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                                           variant=args.variant)
+        fwd_step()
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
         delta = torch.empty_like(lse)
         fwd_flops = flops
         flops = 2.5 * flops   # five matrix products against the forward's two
 
-        def step():
-            fa2.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+        if w.varlen:
+            def step():
+                fa2.bwd_varlen(qd, kd, vd, o, lse, dod, cud, maxlen, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
+                               dv=dv, delta=delta)
+        else:
+            def step():
+                fa2.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                        delta=delta)
 
         if args.fwd_bwd:      # one training step of the attention: the forward, then the backward
             flops += fwd_flops
-            fwd_step = (lambda: fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
-                                        variant=args.variant)) if kd.shape[1] == qd.shape[1] else \
-                (lambda: fa2.fwd_gqa(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
-                                     variant=args.variant))
             bwd_step = step
 
             def step():
@@ -487,9 +494,9 @@ def run(args):
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": (bwd_algorithmic_bytes(w, args.kv_heads or None) if args.bwd
+            "algorithmic_bytes": (bwd_algorithmic_bytes(w, args.kv_heads or None, lengths) if args.bwd
                                   else algorithmic_bytes(w, lengths, args.kv_heads or None)
-                                  + bwd_algorithmic_bytes(w, args.kv_heads or None) if args.fwd_bwd
+                                  + bwd_algorithmic_bytes(w, args.kv_heads or None, lengths) if args.fwd_bwd
                                   else algorithmic_bytes(w, lengths, args.kv_heads or None)),
             "flops_per_launch": flops,
             "kernel_ms": round(ms, 5),

@@ -33,6 +33,9 @@ def test_algorithmic_bytes():
     # backward: read Q, K, V, O, dO and LSE, write dQ, dK, dV, D written and read once
     rows = 16 * 16384
     assert bench.bwd_algorithmic_bytes(w) == 2 * 128 * (4 * rows + 4 * rows) + 12 * rows
+    # varlen backward: the same per token, over all tokens of all sequences
+    vrows = 16 * 30
+    assert bench.bwd_algorithmic_bytes(vl, lengths=[10, 20]) == 2 * 128 * (4 * vrows + 4 * vrows) + 12 * vrows
 
 
 def _write_counters(path, counter, attn_kib, copy_kib):
