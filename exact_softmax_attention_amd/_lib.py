@@ -265,8 +265,11 @@ def fwd_gqa(q, k, v, causal: bool = False, scale: float | None = None, out=None,
 
 
 def fwd_varlen_gqa(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
-                   out=None, lse=None, variant: int = 0):
-    """Packed variable-length grouped-query forward: q [H, T, d], k/v [H_kv, T, d] bf16."""
+                   out=None, lse=None, variant: int | None = None):
+    """Packed variable-length grouped-query forward: q [H, T, d], k/v [H_kv, T, d] bf16.
+
+    Without ``variant`` the call runs the variant ``fa2_fwd_varlen`` picks for d
+    (``varlen_default_variant``)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, torch.bfloat16, 3)
@@ -280,6 +283,8 @@ def fwd_varlen_gqa(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, s
         raise ValueError("cu_seqlens must have at least one entry")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if variant is None:
+        variant = varlen_default_variant(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:

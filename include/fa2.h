@@ -132,7 +132,9 @@ int fa2_fwd_varlen_variant(const void* q, const void* k, const void* v, void* o,
  *   q, o : bf16 [B, H, N, d];  k, v : bf16 [B, H_kv, N, d];  lse : fp32 [B, H, N].
  *   varlen: q, o [H, total_tokens, d]; k, v [H_kv, total_tokens, d]; lse [H, total_tokens].
  *   H_kv must divide H (else FA2_ERR_BAD_SHAPE); H_kv == H is ordinary multi-head attention
- *   and H_kv == 1 is multi-query attention. variant as for fa2_fwd_variant (0 = default).
+ *   and H_kv == 1 is multi-query attention. variant as for fa2_fwd_variant (0 = the
+ *   fixed-length default; for the varlen call, fa2_fwd_varlen_default_variant(d) is the
+ *   variant fa2_fwd_varlen runs).
  * Everything else (validation, ownership, asynchrony, zero-size calls) is as for fa2_fwd.
  */
 int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
