@@ -431,6 +431,13 @@ def run(args):
                             merge_ms=round(merge_ms, 5),
                             merge_roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        # With few query rows (decoding) the step is bound by streaming K and V once: report
+        # that rate for the whole step (pieces and merge).
+        kv_bytes = 2 * w.B * w.H * w.N * w.d * 2
+        kv_gbs = kv_bytes / (ms * 1e-3) / 1e9
+        split_report.update(kv_bytes=kv_bytes,
+                            step_kv_roofline={"bound": "hbm", "achieved": round(kv_gbs, 1), "peak": PEAK_HBM_GBS,
+                                              "unit": "GB/s", "frac": round(kv_gbs / PEAK_HBM_GBS, 4)})
 
     traffic = None
     t = (load_traffic() if (w.name == "long_16k_causal" and args.variant == 0

@@ -61,19 +61,23 @@ def test_chunk_small(d, nq, nk):
 
 @pytest.mark.parametrize("d", [40, 64, 96, 128, 192, 256])
 def test_merge_kernel(d):
-    gen = torch.Generator(device="cpu").manual_seed(600 + d)
-    S, rows = 3, 1000
-    o_parts = torch.randn((S, rows, d), generator=gen).to(torch.bfloat16)
-    lse_parts = torch.randn((S, rows), generator=gen) * 4
-    lse_parts[0, :50] = -float("inf")             # part 0 has no key for these rows
-    lse_parts[:, 50:60] = -float("inf")           # no part has a key for these rows
-    lse_parts[1, 100:110] += 80.0                 # one part dominates
-    o_parts[0, :50] = 0
-    o_parts[:, 50:60] = 0
-    o_ref, l_ref = lse_merge(o_parts.double().numpy(), lse_parts.double().numpy())
-    o, l = fa2.lse_merge(o_parts.to(DEV), lse_parts.to(DEV))
-    torch.cuda.synchronize()
-    _check(_f64(o), _f64(l), o_ref, l_ref, f"merge d{d}")
+    """Both merge kernels: rows spread over lane groups (few parts or many rows) and one
+    workgroup per row (4 or more parts over at most 4096 rows), on either side of the switch."""
+    for S, rows in ((3, 1000), (5, 1000), (64, 37), (200, 5), (4, 4096), (8, 4097)):
+        gen = torch.Generator(device="cpu").manual_seed(600 + d + S)
+        o_parts = torch.randn((S, rows, d), generator=gen).to(torch.bfloat16)
+        lse_parts = torch.randn((S, rows), generator=gen) * 4
+        a, b = rows // 20, rows // 20 + max(rows // 100, 1)
+        lse_parts[0, :a] = -float("inf")            # part 0 has no key for these rows
+        lse_parts[:, a:b] = -float("inf")           # no part has a key for these rows
+        lse_parts[1, b:b + max(rows // 100, 1)] += 80.0   # one part dominates
+        o_parts[0, :a] = 0
+        o_parts[:, a:b] = 0
+        o_ref, l_ref = lse_merge(o_parts.double().numpy(), lse_parts.double().numpy())
+        print(f"[case] merge d={d} parts={S} rows={rows}", flush=True)
+        o, l = fa2.lse_merge(o_parts.to(DEV), lse_parts.to(DEV))
+        torch.cuda.synchronize()
+        _check(_f64(o), _f64(l), o_ref, l_ref, f"merge d{d} S{S} rows{rows}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
