@@ -255,6 +255,22 @@ def test_long_sequence_sampled(d):
             _check(_f64(o[0, h, rows]), _f64(l[0, h, rows]), o_ref, l_ref, f"N{N} d{d} causal{int(causal)} h{h}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_million_token_sampled(d):
+    """One causal head of 2^20 tokens: 16384 key tiles per row block and fp32 running sums
+    over up to 2^20 keys. Sampled rows (first and last rows, tile edges, random rows) against
+    the oracle, computed row by row."""
+    N = 1 << 20
+    q, k, v = make_qkv(1, 1, N, d, seed=36)
+    scale = 1 / math.sqrt(d)
+    print(f"[case] million-token causal d={d}", flush=True)
+    o, l = _run_fixed(q, k, v, True, scale)
+    rows = _sample_rows(N, np.random.default_rng(37), extra=6)
+    o_ref, l_ref = attention_rows(q[0, 0].double().numpy(), k[0, 0].double().numpy(), v[0, 0].double().numpy(),
+                                  True, scale, rows)
+    _check(_f64(o[0, 0, rows]), _f64(l[0, 0, rows]), o_ref, l_ref, f"N{N} d{d} causal")
+
+
 def test_deterministic_and_batch_invariant():
     q, k, v = make_qkv(3, 5, 300, 128, seed=35)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
