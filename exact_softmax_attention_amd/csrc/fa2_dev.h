@@ -50,6 +50,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)LDS_PTR(const void, p);
 }
 
+// This lane's index in its wave, counted from the execution mask with no input register:
+// code that needs it inside a loop can recompute it in two instructions instead of keeping
+// the thread id live (or spilled) across the loop.
+__device__ __forceinline__ int wave_lane() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 // Maximum over both 32-lane halves (lane l and l^32 hold the two halves of a row's keys).
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

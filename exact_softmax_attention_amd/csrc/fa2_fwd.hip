@@ -407,8 +407,12 @@ __device__ __forceinline__ void fwd_block(const Params& p, int id) {
     // It is dead when koffs - 4*hl exceeds thr (causal: key > query; ragged: key >= length),
     // a per-lane threshold; the sign of thr - const selects -inf with one bitfield insert.
     if ((CAUSAL && key0 + BC - 1 > qw0 + diag) || key0 + BC > seq_k) {
-      int thr = seq_k - 1 - key0 - 4 * hl;
-      if (CAUSAL) thr = min(thr, qrow + diag - key0 - 4 * hl);
+      // The lane-derived terms are taken afresh here: kept from the thread id they would
+      // stay live across the tile loop, only for the diagonal and ragged tiles.
+      const int ln = wave_lane();
+      const int hm = ln >> 5;
+      int thr = seq_k - 1 - key0 - 4 * hm;
+      if (CAUSAL) thr = min(thr, qw0 + (ln & 31) + diag - key0 - 4 * hm);
 #pragma unroll
       for (int kb = 0; kb < TL::NKB; ++kb)
 #pragma unroll
