@@ -51,11 +51,17 @@ CLOCK_SECONDS = 1.0    # untimed steps after the timed ones while amd-smi sample
 
 
 def kernel_source_hash() -> str:
-    """Hash of the forward kernel's sources (the kernel file and the device helpers it includes)."""
+    """Hash of the forward kernel's code (the kernel file and the device helpers it includes),
+    with `//` comments, trailing blanks and empty lines left out, so that an edit to a comment
+    does not mark the stored counters as stale. The sources use no `/* */` comments and no
+    `//` inside string literals."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

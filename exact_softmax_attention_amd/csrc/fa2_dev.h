@@ -50,9 +50,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)LDS_PTR(const void, p);
 }
 
-// This lane's index in its wave, counted from the execution mask with no input register:
-// code that needs it inside a loop can recompute it in two instructions instead of keeping
-// the thread id live (or spilled) across the loop.
+// This lane's index in its wave: mbcnt counts the set bits of an all-ones mask below the
+// lane. It takes no input register, so code that needs it inside a loop can recompute it in
+// two instructions instead of keeping the thread id live (or spilled) across the loop.
 __device__ __forceinline__ int wave_lane() {
   return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
