@@ -42,6 +42,8 @@ _SIGNATURES = {
     "fa2_lse_merge": ([_c_void_p, _c_void_p, _c_int, ctypes.c_longlong, _c_int, _c_void_p, _c_void_p, _c_void_p],
                       _c_int),
     "fa2_bwd": ([_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
+    "fa2_bwd_ws": ([_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p, ctypes.c_longlong, _c_void_p], _c_int),
+    "fa2_bwd_workspace_bytes": ([_c_int] * 6, ctypes.c_longlong),
     "fa2_bwd_varlen": ([_c_void_p] * 11 + [_c_int] * 7 + [_c_float, _c_void_p], _c_int),
     "fa2_num_variants": ([_c_int], _c_int),
     "fa2_fwd_geometry": ([_c_int] * 6 + [ctypes.POINTER(_c_int)] * 4, _c_int),
@@ -304,12 +306,15 @@ def fwd_varlen_gqa(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, s
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-        dq=None, dk=None, dv=None, delta=None):
+        dq=None, dk=None, dv=None, delta=None, split: bool = True):
     """Gradients (dq, dk, dv) of the forward for upstream gradient ``dout``.
 
     q, o, dout: bf16 [B, H, N, d]; k, v: bf16 [B, H_kv, N, d] (H_kv divides H); lse: fp32
     [B, H, N] from the forward with the same ``scale``. ``delta`` (fp32 [B, H, N]) is the
     scratch buffer for D = rowsum(dout * o); outputs and scratch are allocated when not given.
+    With grouped- or multi-query heads and ``split`` (the default) the call goes to
+    fa2_bwd_ws, which spreads each group's query heads over several dK/dV workgroups, with
+    the workspace it asks for allocated here; ``split=False`` calls fa2_bwd.
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -335,10 +340,16 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
         raise ValueError("delta must be [B, H, N]")
     _same_device(q, k, v, o, lse, dout, dq, dk, dv, delta)
     lib = load_library()
+    ws_bytes = lib.fa2_bwd_workspace_bytes(B, H, H_kv, N, d, int(bool(causal))) if split and H_kv != H else 0
     with torch.cuda.device(q.device):
-        st = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                         B, H, H_kv, N, d, int(bool(causal)), float(scale), _stream_ptr(q.device))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                B, H, H_kv, N, d, int(bool(causal)), float(scale))
+        if ws_bytes > 0:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            st = lib.fa2_bwd_ws(*args, ws.data_ptr(), ws_bytes, _stream_ptr(q.device))
+        else:
+            st = lib.fa2_bwd(*args, _stream_ptr(q.device))
     _check(st)
     return dq, dk, dv
 

@@ -49,6 +49,8 @@
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -70,6 +72,10 @@ struct BwdParams {
   int T;                  // tokens per head plane: N, or total_tokens (varlen)
   int nblk;               // 128-row (dQ) or 128-key (dK/dV) blocks per sequence
   int heads_per_xcd;      // > 0: XCD-aware workgroup order
+  int hsplit;             // dK/dV: workgroups per (key/value head, key block), each taking
+                          // g / hsplit query heads of the group; 1 = the whole group
+  float* kv_ws;           // hsplit > 1: fp32 partial dK, dV per split, [hsplit][2][ws_slab]
+  long long ws_slab;      // elements of one partial (key/value rows x dg)
   float c;                // |scale| * log2(e), at least 1e-30
   float scale;            // the signed softmax scale
   uint32_t qflip;         // 0x80008000 negates Q in the score products (scale < 0), else 0
@@ -456,8 +462,13 @@ __device__ __forceinline__ void bwd_dkdv_block(const BwdParams& p, int id) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  int bk, jb;
-  decode_bwd<CAUSAL, false>(id, p.nb * p.Hkv, p.nblk, p.heads_per_xcd, bk, jb);
+  // Work item: (batch or sequence, key/value head, query-head split) x key block. The splits
+  // of one key/value head are adjacent, so they share an XCD and the heaviest-first order.
+  int bks, jb;
+  decode_bwd<CAUSAL, false>(id, p.nb * p.Hkv * p.hsplit, p.nblk, p.heads_per_xcd, bks, jb);
+  const int bk = bks / p.hsplit;
+  const int sp = bks - bk * p.hsplit;   // this split's query heads: [sp * gs, sp * gs + gs)
+  const int gs = p.g / p.hsplit;
   const int bi = bk / p.Hkv;
   const int hk = bk - bi * p.Hkv;
   int tok0, seq_len;
@@ -485,10 +496,10 @@ __device__ __forceinline__ void bwd_dkdv_block(const BwdParams& p, int id) {
     vf[kc] = as_bf16x8(tv);
   }
 
-  // Query tiles: causal starts at the tile holding query k0; every query head of the group.
+  // Query tiles: causal starts at the tile holding query k0; every query head of the split.
   const int t0 = CAUSAL ? k0 / BQ : 0;
   const int ntq = (seq_len + BQ - 1) / BQ - t0;
-  const int nsteps = ntq * p.g;
+  const int nsteps = ntq * gs;
 
   int drow_[TL::DMA_PER_WAVE];
   uint32_t doff[TL::DMA_PER_WAVE];
@@ -504,7 +515,7 @@ __device__ __forceinline__ void bwd_dkdv_block(const BwdParams& p, int id) {
   auto step_coords = [&](int s, int& q0, size_t& qrow0) {
     const int hq = s / ntq;
     q0 = (t0 + (s - hq * ntq)) * BQ;
-    qrow0 = q_plane<VARLEN>(p, bi, hk * p.g + hq) + (size_t)tok0;
+    qrow0 = q_plane<VARLEN>(p, bi, hk * p.g + sp * gs + hq) + (size_t)tok0;
   };
   auto dma_step = [&](int s, unsigned char* stage) {
     int q0;
@@ -692,7 +703,23 @@ __device__ __forceinline__ void bwd_dkdv_block(const BwdParams& p, int id) {
     if (st + 1 < nsteps) iteration(st + 1, lds1, lds0);
   }
 
-  if (kvalid) {
+  if (kvalid && p.hsplit > 1) {
+    // This split's share of the sums over the group: fp32 partials, added up in split order
+    // by fa2_bwd_kv_reduce_kernel.
+    float* kw = p.kv_ws + (size_t)sp * 2 * (size_t)p.ws_slab + (kvrow0 + (size_t)krow) * dg;
+    float* vw = kw + p.ws_slab;
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (db * 32 + 8 * g + 4 * hl < dg) {
+          const int c = db * 32 + 8 * g + 4 * hl;
+          *(f32x4*)(kw + c) = (f32x4){dkacc[db][4 * g + 0] * p.scale, dkacc[db][4 * g + 1] * p.scale,
+                                      dkacc[db][4 * g + 2] * p.scale, dkacc[db][4 * g + 3] * p.scale};
+          *(f32x4*)(vw + c) = (f32x4){dvacc[db][4 * g + 0], dvacc[db][4 * g + 1],
+                                      dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
+        }
+  } else if (kvalid) {
     uint16_t* kout = p.dk + (kvrow0 + (size_t)krow) * dg;
     uint16_t* vout = p.dv + (kvrow0 + (size_t)krow) * dg;
 #pragma unroll
@@ -723,6 +750,24 @@ void fa2_bwd_dkdv_kernel_persist(BwdParams p, unsigned int* ctr, int total) {
                  [&](int id) { bwd_dkdv_block<D, BQ, CAUSAL, VARLEN, NW, KLDS, LA_, LA_ACC, true>(p, id); });
 }
 
+// Sum of the query-head splits' partial dK and dV, in split order (fixed, so the bits do not
+// depend on timing), rounded to bf16 as the unsplit epilogue rounds. Thread i handles
+// elements [4i, 4i + 4) of both; slab is a multiple of 8.
+__global__ __launch_bounds__(256) void fa2_bwd_kv_reduce_kernel(const float* __restrict__ ws, long long slab,
+                                                                int nsplit, uint16_t* __restrict__ dk,
+                                                                uint16_t* __restrict__ dv) {
+  const long long e = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
+  if (e >= slab) return;
+  f32x4 ak = *(const f32x4*)(ws + e);
+  f32x4 av = *(const f32x4*)(ws + slab + e);
+  for (int s = 1; s < nsplit; ++s) {
+    ak += *(const f32x4*)(ws + (size_t)s * 2 * (size_t)slab + e);
+    av += *(const f32x4*)(ws + (size_t)s * 2 * (size_t)slab + slab + e);
+  }
+  *(u32x2*)(dk + e) = (u32x2){pack_bf16x2(ak[0], ak[1]), pack_bf16x2(ak[2], ak[3])};
+  *(u32x2*)(dv + e) = (u32x2){pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+}
+
 // ---- host side ------------------------------------------------------------------------
 
 typedef const void* KernelFn;
@@ -733,6 +778,7 @@ struct BwdKernels {
   int dq_threads;
   int dkdv_threads;
   int dkdv_bk;           // keys per dK/dV workgroup
+  int dkdv_occ;          // dK/dV waves per SIMD
   KernelFn dq[2][2];     // [varlen][causal]
   KernelFn dkdv[2][2];
   // Persistent forms, taken by varlen calls outside graph capture: workgroups per CU (0: none)
@@ -752,6 +798,7 @@ BwdKernels make_bwd() {
   k.dq_threads = DqTile<D, BC_DQ, NW_DQ>::THREADS;
   k.dkdv_threads = DkvTile<D, BQ_DKDV, NW_DKDV>::THREADS;
   k.dkdv_bk = DkvTile<D, BQ_DKDV, NW_DKDV>::BK;
+  k.dkdv_occ = OCC_DKDV;
   k.dq[0][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, false, NW_DQ, OCC_DQ, LA_DQ>;
   k.dq[0][1] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, true, false, NW_DQ, OCC_DQ, LA_DQ>;
   k.dq[1][0] = (KernelFn)&fa2_bwd_dq_kernel<D, BC_DQ, false, true, NW_DQ, OCC_DQ, LA_DQ>;
@@ -793,6 +840,24 @@ const BwdKernels* bwd_kernels(int d) {
 }
 
 bool aligned_to(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+// Query-head splits of the dK/dV kernel in a fixed-length call with grouped- or multi-query
+// heads. Unsplit, the kernel has one wave per 32 keys of each key/value head, which leaves
+// SIMDs idle when there are few key/value heads (B=1, H_kv=2, N=16384: 1024 waves, where two
+// per SIMD of the 256 CUs take 2048). Causal key blocks carry unequal work (the first sees
+// every query, the last one tile), so there the kernel needs about four waves per slot for
+// the heaviest-first order to even them out; with one per slot the heaviest block sets the
+// time (measured: two splits, one wave per slot, 615 TFLOP/s against 837 without groups).
+// Returns the smallest divisor S of g that gives at least occ waves per SIMD (four times
+// that when causal), else g; 1 when g == 1.
+constexpr long long kBwdSimds = 1024;   // 256 CUs x 4 SIMDs
+int bwd_head_split(long long B, int H_kv, int g, int N, int occ, bool causal) {
+  const long long waves = B * H_kv * (((long long)N + 31) / 32);
+  const long long target = kBwdSimds * occ * (causal ? 4 : 1);
+  for (int S = 1; S < g; ++S)
+    if (g % S == 0 && waves * S >= target) return S;
+  return g;
+}
 
 // Head dimensions of the backward: multiples of 8 up to 256, run on the D = 64, 128 or 256
 // kernels with padded columns as in the forward. Q, O, dO, K and V padded columns are either zero in
@@ -849,9 +914,15 @@ int bwd_launch(const BwdKernels& kk, bool varlen, bool causal, BwdParams p, int 
   if (st != FA2_OK) return st;
   BwdParams p2 = p;
   p2.nblk = nblk_k;
-  p2.heads_per_xcd = (!varlen && npairs_k % 8 == 0) ? (int)(npairs_k / 8) : 0;
-  return bwd_kernel_launch(kk.dkdv[v][c], persist ? kk.dkdv_persist[c] : nullptr, kk.dkdv_wg_per_cu,
-                           kk.dkdv_threads, p2, nblk_k * npairs_k, dev, stream);
+  const long long items_k = npairs_k * p.hsplit;   // (pair, split) work items per key block
+  p2.heads_per_xcd = (!varlen && items_k % 8 == 0) ? (int)(items_k / 8) : 0;
+  st = bwd_kernel_launch(kk.dkdv[v][c], persist ? kk.dkdv_persist[c] : nullptr, kk.dkdv_wg_per_cu,
+                         kk.dkdv_threads, p2, nblk_k * items_k, dev, stream);
+  if (st != FA2_OK || p.hsplit == 1) return st;
+  const long long nthr = p.ws_slab / 4;
+  hipLaunchKernelGGL(fa2_bwd_kv_reduce_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, (const float*)p.kv_ws, p.ws_slab, p.hsplit, p.dk, p.dv);
+  return hipGetLastError() == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
 int bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -880,18 +951,19 @@ void bwd_fill(BwdParams& p, const void* q, const void* k, const void* v, const v
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
   p.delta = delta;
+  p.hsplit = 1;
+  p.kv_ws = nullptr;
+  p.ws_slab = 0;
   p.c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
   p.scale = scale;
   p.qflip = scale < 0.f ? 0x80008000u : 0u;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-            const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int H_kv,
-            int N, int d, int causal, float scale, void* stream) {
+// Fixed-length backward; split allows query-head splits of the dK/dV kernel (fa2_bwd_ws).
+int bwd_fixed(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int H_kv,
+              int N, int d, int causal, float scale, bool split, void* workspace,
+              long long workspace_bytes, void* stream) {
   if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N < 0) return FA2_ERR_BAD_SHAPE;
   if (N == 0) return bwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
   int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
@@ -899,6 +971,14 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   const long long nblk = ((long long)N + 127) / 128;   // most blocks any kernel launches
   const long long pq = (long long)B * H, pk = (long long)B * H_kv;
   if (nblk * pq > 0x7fffffffLL || pq * (long long)N > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
+  const int S = split ? bwd_head_split(B, H_kv, H / H_kv, N, kk.dkdv_occ, causal != 0) : 1;
+  const long long slab = pk * (long long)N * d;         // elements of dK (or dV)
+  if (S > 1) {
+    if (!workspace) return FA2_ERR_NULL_PTR;
+    if (!aligned_to(workspace, 16)) return FA2_ERR_MISALIGNED;
+    if (workspace_bytes < (long long)S * 2 * slab * (long long)sizeof(float)) return FA2_ERR_SCRATCH_TOO_SMALL;
+  }
   BwdParams p;
   bwd_fill(p, q, k, v, o, lse, dout, dq, dk, dv, delta, scale);
   p.cu_seqlens = nullptr;
@@ -909,10 +989,39 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.g = H / H_kv;
   p.N = N;
   p.T = N;
-  const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
+  p.hsplit = S;
+  p.kv_ws = S > 1 ? (float*)workspace : nullptr;
+  p.ws_slab = S > 1 ? slab : 0;
   const long long nblk_q = ((long long)N + kk.dq_br - 1) / kk.dq_br;
   const long long nblk_k = ((long long)N + kk.dkdv_bk - 1) / kk.dkdv_bk;
+  if (nblk_k * pk * S > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
   return bwd_launch(kk, false, causal != 0, p, (int)nblk_q, (int)nblk_k, pq, pk, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+long long fa2_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, int causal) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N <= 0 || !bwd_head_dim(d)) return 0;
+  const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
+  const int S = bwd_head_split(B, H_kv, H / H_kv, N, kk.dkdv_occ, causal != 0);
+  return S > 1 ? (long long)S * 2 * B * H_kv * (long long)N * d * (long long)sizeof(float) : 0;
+}
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int H_kv,
+            int N, int d, int causal, float scale, void* stream) {
+  return bwd_fixed(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, causal, scale, false,
+                   nullptr, 0, stream);
+}
+
+int fa2_bwd_ws(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int H_kv,
+               int N, int d, int causal, float scale, void* workspace, long long workspace_bytes,
+               void* stream) {
+  return bwd_fixed(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, causal, scale, true,
+                   workspace, workspace_bytes, stream);
 }
 
 int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -261,6 +261,36 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
                    const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
                    int H, int H_kv, int d, int causal, float scale, void* stream);
 
+/*
+ * Backward of a fixed-length call with the query heads of each group split over several
+ * dK/dV workgroups, for grouped- and multi-query attention. The gradients of a key/value head
+ * are sums over the query heads that share it (chlience notes, section 5.6); fa2_bwd forms
+ * them in one dK/dV workgroup per (key/value head, 128-key block), which with few key/value
+ * heads leaves the GPU half idle (B=1, H_kv=2, N=16384: 1024 waves, where two per SIMD take
+ * 2048). Here each group's g query heads are split over S workgroups, S the smallest divisor
+ * of g that gives the dK/dV kernel as many waves as its occupancy fills on 256 CUs, four
+ * times that when causal (causal key blocks carry unequal work), else g.
+ * Each split writes fp32 partial dK and dV to the workspace, and a third kernel adds them in
+ * split order and rounds to bf16.
+ *   Arguments and results as fa2_bwd, plus:
+ *   workspace       : device memory, 16-byte aligned, caller-owned, overwritten; may be NULL
+ *                     when fa2_bwd_workspace_bytes(B, H, H_kv, N, d, causal) is 0.
+ *   workspace_bytes : its size; below fa2_bwd_workspace_bytes(): FA2_ERR_SCRATCH_TOO_SMALL
+ *                     (NULL when needed: FA2_ERR_NULL_PTR; misaligned: FA2_ERR_MISALIGNED).
+ * When no split is needed (H_kv == H, or enough key/value heads and keys) the call is fa2_bwd,
+ * bit for bit. With a split, dK and dV are the same sums taken in another order, so their
+ * bits can differ from fa2_bwd's within rounding; repeated calls give the same bits.
+ */
+int fa2_bwd_ws(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int H_kv,
+               int N, int d, int causal, float scale, void* workspace, long long workspace_bytes,
+               void* stream);
+
+/* Workspace bytes fa2_bwd_ws needs for this shape and mask: S * 2 * B * H_kv * N * d * 4
+ * (fp32 partial dK and dV per split), 0 when it does not split or the shape is invalid. Host
+ * only; touches no device. */
+long long fa2_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, int causal);
+
 /* Number of kernel variants for head dimension d (0 if d is unsupported; a padded d has
  * the variants of its padded width). Host only. */
 int fa2_num_variants(int d);

@@ -296,6 +296,44 @@ def test_bwd_empty_is_ok():
     assert _bwd_varlen(T=0, cu=None, **none) == 0
 
 
+def _bwd_ws(ws=FAKE, nbytes=1 << 40, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+            delta=FAKE, B=1, H=8, H_kv=2, N=64, d=128, causal=1, scale=0.088):
+    return fa2.load_library().fa2_bwd_ws(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, H_kv, N, d, causal, scale,
+                                          ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(ws=None), 1), (dict(ws=FAKE + 8), 4), (dict(nbytes=0), 10), (dict(nbytes=-1), 10),
+    (dict(q=None), 1), (dict(H_kv=3), 2), (dict(d=100), 3), (dict(dk=FAKE + 2), 4),
+    (dict(scale=float("nan")), 5),
+])
+def test_bwd_ws_validation(kwargs, code):
+    """Every case fails before any launch: the workspace is needed for this shape (H=8 over
+    H_kv=2, 64 keys) and checked after the tensors."""
+    assert _bwd_ws(**kwargs) == code
+
+
+def test_bwd_workspace_bytes():
+    """Query-head splits: the smallest divisor S of g that gives the dK/dV kernel (one wave
+    per 32 keys of each key/value head and split) its waves per SIMD on 1024 SIMDs (two at
+    d = 128, three at d = 64; four times as many when causal), else g; S * 2 * B * H_kv * N * d
+    fp32 values when S > 1."""
+    f = fa2.load_library().fa2_bwd_workspace_bytes
+    for causal in (0, 1):
+        assert f(1, 16, 16, 16384, 128, causal) == 0                   # no groups
+        assert f(1, 8, 2, 300, 64, causal) == 4 * 2 * 1 * 2 * 300 * 64 * 4  # S = g = 4
+    assert f(1, 16, 2, 16384, 128, 0) == 2 * 2 * 1 * 2 * 16384 * 128 * 4   # 1024 waves -> S = 2
+    assert f(1, 16, 2, 16384, 128, 1) == 8 * 2 * 1 * 2 * 16384 * 128 * 4   # causal: S = 8
+    assert f(1, 16, 1, 16384, 128, 0) == 4 * 2 * 1 * 1 * 16384 * 128 * 4   # 512 waves -> S = 4
+    assert f(1, 16, 1, 16384, 128, 1) == 16 * 2 * 1 * 1 * 16384 * 128 * 4
+    assert f(8, 16, 2, 2048, 128, 0) == 2 * 2 * 8 * 2 * 2048 * 128 * 4
+    assert f(16, 16, 2, 4096, 128, 0) == 0                               # 4096 waves already
+    assert f(16, 16, 2, 4096, 128, 1) == 2 * 2 * 16 * 2 * 4096 * 128 * 4
+    assert f(1, 12, 4, 1000, 96, 0) == 3 * 2 * 1 * 4 * 1000 * 96 * 4       # g = 3, padded d
+    for bad in ((0, 8, 2, 64, 64), (1, 6, 4, 64, 64), (1, 8, 2, 0, 64), (1, 8, 2, 64, 100), (1, 8, 0, 64, 64)):
+        assert f(*bad, 1) == 0
+
+
 def _chunk(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, H_kv=2, Nq=16, Nk=32, d=64, causal=1, diag=0,
            scale=0.125, variant=0):
     return fa2.load_library().fa2_fwd_chunk(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, causal, diag, scale, variant,
