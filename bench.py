@@ -228,16 +228,25 @@ def run(args):
     # fa2_fwd_varlen); another variant through the *_variant calls.
     entry_variant = None if args.variant == 0 else args.variant
     if w.varlen:
-        q, k, v, cu, lengths = workload_inputs(w)
+        if args.kv_heads:
+            from synthetic import make_varlen
+            if w.H % args.kv_heads:
+                raise SystemExit(f"--kv-heads {args.kv_heads} must divide H={w.H}")
+            q, k, v, cu, lengths = make_varlen(w.H, w.d, w.seed, num_seqs=w.num_seqs, min_len=w.min_len,
+                                               max_len=w.max_len, k_scale=w.k_scale, H_kv=args.kv_heads)
+        else:
+            q, k, v, cu, lengths = workload_inputs(w)
         qd, kd, vd, cud = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
         o = torch.empty_like(qd)
         lse = torch.empty(qd.shape[:2], dtype=torch.float32, device=dev)
         maxlen = max(lengths)
         flops = varlen_metric_flops(lengths, w.H, w.d, w.causal)
 
+        varlen_fwd = fa2.fwd_varlen_gqa if args.kv_heads else fa2.fwd_varlen
+
         def step():
-            fa2.fwd_varlen(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o, lse=lse,
-                           variant=entry_variant)
+            varlen_fwd(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                       variant=entry_variant)
     elif args.kv_heads:
         from synthetic import make_qkv
         if w.H % args.kv_heads:
@@ -298,8 +307,8 @@ def run(args):
         gen = torch.Generator(device="cpu").manual_seed(1000 + w.seed)
         dod = torch.randn(qd.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).to(dev)
         if w.varlen:
-            fwd_step = lambda: fa2.fwd_varlen(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o,
-                                              lse=lse, variant=entry_variant)
+            fwd_step = lambda: varlen_fwd(qd, kd, vd, cud, maxlen, causal=w.causal, scale=w.scale, out=o,
+                                          lse=lse, variant=entry_variant)
         elif kd.shape[1] == qd.shape[1]:
             fwd_step = lambda: fa2.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
                                        variant=entry_variant)

@@ -44,6 +44,9 @@ _SIGNATURES = {
     "fa2_bwd": ([_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p], _c_int),
     "fa2_bwd_ws": ([_c_void_p] * 10 + [_c_int] * 6 + [_c_float, _c_void_p, ctypes.c_longlong, _c_void_p], _c_int),
     "fa2_bwd_workspace_bytes": ([_c_int] * 6, ctypes.c_longlong),
+    "fa2_bwd_varlen_ws": ([_c_void_p] * 11 + [_c_int] * 7 + [_c_float, _c_void_p, ctypes.c_longlong, _c_void_p],
+                          _c_int),
+    "fa2_bwd_varlen_workspace_bytes": ([_c_int] * 7, ctypes.c_longlong),
     "fa2_bwd_varlen": ([_c_void_p] * 11 + [_c_int] * 7 + [_c_float, _c_void_p], _c_int),
     "fa2_num_variants": ([_c_int], _c_int),
     "fa2_fwd_geometry": ([_c_int] * 6 + [ctypes.POINTER(_c_int)] * 4, _c_int),
@@ -355,8 +358,10 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
 
 
 def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool = False,
-               scale: float | None = None, dq=None, dk=None, dv=None, delta=None):
-    """Packed variable-length backward: q, o, dout [H, T, d]; k, v [H_kv, T, d]; lse [H, T]."""
+               scale: float | None = None, dq=None, dk=None, dv=None, delta=None, split: bool = True):
+    """Packed variable-length backward: q, o, dout [H, T, d]; k, v [H_kv, T, d]; lse [H, T].
+    Grouped heads with ``split`` go to fa2_bwd_varlen_ws (workspace allocated here), as in
+    ``bwd``."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tensor(name, t, torch.bfloat16, 3)
@@ -385,11 +390,18 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool 
         raise ValueError("delta must be [H, T]")
     _same_device(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, delta)
     lib = load_library()
+    ws_bytes = (lib.fa2_bwd_varlen_workspace_bytes(num_seqs, int(max_seqlen), T, H, H_kv, d, int(bool(causal)))
+                if split and H_kv != H else 0)
     with torch.cuda.device(q.device):
-        st = lib.fa2_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                                cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, H_kv, d,
-                                int(bool(causal)), float(scale), _stream_ptr(q.device))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                cu_seqlens.data_ptr(), num_seqs, int(max_seqlen), T, H, H_kv, d,
+                int(bool(causal)), float(scale))
+        if ws_bytes > 0:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            st = lib.fa2_bwd_varlen_ws(*args, ws.data_ptr(), ws_bytes, _stream_ptr(q.device))
+        else:
+            st = lib.fa2_bwd_varlen(*args, _stream_ptr(q.device))
     _check(st)
     return dq, dk, dv
 

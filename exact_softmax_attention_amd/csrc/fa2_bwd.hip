@@ -768,6 +768,32 @@ __global__ __launch_bounds__(256) void fa2_bwd_kv_reduce_kernel(const float* __r
   *(u32x2*)(dv + e) = (u32x2){pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
 }
 
+// Varlen form of the reduce: workgroup (sequence, key/value head, 128-row block) adds up the
+// rows of that sequence only, so tokens that no sequence covers stay unwritten in dK and dV
+// (and their workspace rows, which no split wrote, are never read).
+__global__ __launch_bounds__(256) void fa2_bwd_kv_reduce_varlen_kernel(BwdParams p) {
+  const int rb = blockIdx.x, bk = blockIdx.y;
+  const int bi = bk / p.Hkv, hk = bk - bi * p.Hkv;
+  int tok0, len;
+  seq_range<true>(p, bi, tok0, len);
+  const int r0 = rb * 128;
+  if (r0 >= len) return;
+  const int rows = min(128, len - r0);
+  const int c4 = p.dg / 4;                    // float4 groups per row
+  const size_t base = (kv_plane<true>(p, bi, hk) + (size_t)tok0 + (size_t)r0) * (size_t)p.dg;
+  for (int t = threadIdx.x; t < rows * c4; t += 256) {
+    const size_t e = base + (size_t)(t / c4) * (size_t)p.dg + (size_t)(t % c4) * 4;
+    f32x4 ak = *(const f32x4*)(p.kv_ws + e);
+    f32x4 av = *(const f32x4*)(p.kv_ws + p.ws_slab + e);
+    for (int s = 1; s < p.hsplit; ++s) {
+      ak += *(const f32x4*)(p.kv_ws + (size_t)s * 2 * (size_t)p.ws_slab + e);
+      av += *(const f32x4*)(p.kv_ws + (size_t)s * 2 * (size_t)p.ws_slab + p.ws_slab + e);
+    }
+    *(u32x2*)(p.dk + e) = (u32x2){pack_bf16x2(ak[0], ak[1]), pack_bf16x2(ak[2], ak[3])};
+    *(u32x2*)(p.dv + e) = (u32x2){pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+  }
+}
+
 // ---- host side ------------------------------------------------------------------------
 
 typedef const void* KernelFn;
@@ -919,9 +945,14 @@ int bwd_launch(const BwdKernels& kk, bool varlen, bool causal, BwdParams p, int 
   st = bwd_kernel_launch(kk.dkdv[v][c], persist ? kk.dkdv_persist[c] : nullptr, kk.dkdv_wg_per_cu,
                          kk.dkdv_threads, p2, nblk_k * items_k, dev, stream);
   if (st != FA2_OK || p.hsplit == 1) return st;
-  const long long nthr = p.ws_slab / 4;
-  hipLaunchKernelGGL(fa2_bwd_kv_reduce_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, (const float*)p.kv_ws, p.ws_slab, p.hsplit, p.dk, p.dv);
+  if (varlen) {
+    hipLaunchKernelGGL(fa2_bwd_kv_reduce_varlen_kernel, dim3((unsigned)((p.N + 127) / 128), (unsigned)npairs_k),
+                       dim3(256), 0, (hipStream_t)stream, p);
+  } else {
+    const long long nthr = p.ws_slab / 4;
+    hipLaunchKernelGGL(fa2_bwd_kv_reduce_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, (const float*)p.kv_ws, p.ws_slab, p.hsplit, p.dk, p.dv);
+  }
   return hipGetLastError() == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
@@ -998,6 +1029,51 @@ int bwd_fixed(const void* q, const void* k, const void* v, const void* o, const 
   return bwd_launch(kk, false, causal != 0, p, (int)nblk_q, (int)nblk_k, pq, pk, stream);
 }
 
+// Varlen backward; split allows query-head splits of the dK/dV kernel (fa2_bwd_varlen_ws).
+int bwd_varlen_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, float* delta,
+                    const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens, int H,
+                    int H_kv, int d, int causal, float scale, bool split, void* workspace,
+                    long long workspace_bytes, void* stream) {
+  if (H <= 0 || H_kv <= 0 || H % H_kv != 0 || num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
+    return FA2_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
+    return bwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
+  if (!cu_seqlens) return FA2_ERR_NULL_PTR;
+  if (!aligned_to(cu_seqlens, 4)) return FA2_ERR_MISALIGNED;
+  int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
+  if (st != FA2_OK) return st;
+  const long long nblk = ((long long)max_seqlen + 127) / 128;   // most blocks any kernel launches
+  const long long pq = (long long)num_seqs * H, pk = (long long)num_seqs * H_kv;
+  if (nblk * pq > 0x7fffffffLL || (long long)H * total_tokens > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  BwdParams p;
+  bwd_fill(p, q, k, v, o, lse, dout, dq, dk, dv, delta, scale);
+  p.cu_seqlens = cu_seqlens;
+  p.nb = num_seqs;
+  p.dg = d;
+  p.H = H;
+  p.Hkv = H_kv;
+  p.g = H / H_kv;
+  p.N = max_seqlen;
+  p.T = total_tokens;
+  const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
+  const int S = split ? bwd_head_split(1, H_kv, H / H_kv, total_tokens, kk.dkdv_occ, causal != 0) : 1;
+  const long long slab = (long long)H_kv * total_tokens * d;
+  if (S > 1) {
+    if (!workspace) return FA2_ERR_NULL_PTR;
+    if (!aligned_to(workspace, 16)) return FA2_ERR_MISALIGNED;
+    if (workspace_bytes < (long long)S * 2 * slab * (long long)sizeof(float)) return FA2_ERR_SCRATCH_TOO_SMALL;
+  }
+  p.hsplit = S;
+  p.kv_ws = S > 1 ? (float*)workspace : nullptr;
+  p.ws_slab = S > 1 ? slab : 0;
+  const long long nblk_q = ((long long)max_seqlen + kk.dq_br - 1) / kk.dq_br;
+  const long long nblk_k = ((long long)max_seqlen + kk.dkdv_bk - 1) / kk.dkdv_bk;
+  if (nblk_k * pk * S > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
+  return bwd_launch(kk, true, causal != 0, p, (int)nblk_q, (int)nblk_k, pq, pk, stream);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -1028,31 +1104,28 @@ int fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
                    const void* dout, void* dq, void* dk, void* dv, float* delta,
                    const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens, int H,
                    int H_kv, int d, int causal, float scale, void* stream) {
-  if (H <= 0 || H_kv <= 0 || H % H_kv != 0 || num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
-    return FA2_ERR_BAD_SHAPE;
-  if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0)
-    return bwd_head_dim(d) ? FA2_OK : FA2_ERR_UNSUPPORTED_HEADDIM;
-  if (!cu_seqlens) return FA2_ERR_NULL_PTR;
-  if (!aligned_to(cu_seqlens, 4)) return FA2_ERR_MISALIGNED;
-  int st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, delta, d, scale);
-  if (st != FA2_OK) return st;
-  const long long nblk = ((long long)max_seqlen + 127) / 128;   // most blocks any kernel launches
-  const long long pq = (long long)num_seqs * H, pk = (long long)num_seqs * H_kv;
-  if (nblk * pq > 0x7fffffffLL || (long long)H * total_tokens > 0x7fffffffLL) return FA2_ERR_TOO_LARGE;
-  BwdParams p;
-  bwd_fill(p, q, k, v, o, lse, dout, dq, dk, dv, delta, scale);
-  p.cu_seqlens = cu_seqlens;
-  p.nb = num_seqs;
-  p.dg = d;
-  p.H = H;
-  p.Hkv = H_kv;
-  p.g = H / H_kv;
-  p.N = max_seqlen;
-  p.T = total_tokens;
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, delta, cu_seqlens, num_seqs, max_seqlen,
+                         total_tokens, H, H_kv, d, causal, scale, false, nullptr, 0, stream);
+}
+
+long long fa2_bwd_varlen_workspace_bytes(int num_seqs, int max_seqlen, int total_tokens, int H, int H_kv,
+                                         int d, int causal) {
+  if (num_seqs <= 0 || max_seqlen <= 0 || total_tokens <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 ||
+      !bwd_head_dim(d))
+    return 0;
   const BwdKernels& kk = *bwd_kernels(bwd_padded_dim(d));
-  const long long nblk_q = ((long long)max_seqlen + kk.dq_br - 1) / kk.dq_br;
-  const long long nblk_k = ((long long)max_seqlen + kk.dkdv_bk - 1) / kk.dkdv_bk;
-  return bwd_launch(kk, true, causal != 0, p, (int)nblk_q, (int)nblk_k, pq, pk, stream);
+  // T keys per key/value head stand in for the sequences' keys (equal when cu covers all tokens).
+  const int S = bwd_head_split(1, H_kv, H / H_kv, total_tokens, kk.dkdv_occ, causal != 0);
+  return S > 1 ? (long long)S * 2 * H_kv * (long long)total_tokens * d * (long long)sizeof(float) : 0;
+}
+
+int fa2_bwd_varlen_ws(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* delta,
+                      const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens, int H,
+                      int H_kv, int d, int causal, float scale, void* workspace, long long workspace_bytes,
+                      void* stream) {
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, delta, cu_seqlens, num_seqs, max_seqlen,
+                         total_tokens, H, H_kv, d, causal, scale, true, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -291,6 +291,21 @@ int fa2_bwd_ws(const void* q, const void* k, const void* v, const void* o, const
  * only; touches no device. */
 long long fa2_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, int causal);
 
+/*
+ * The same query-head splits for packed variable-length batches: arguments and results as
+ * fa2_bwd_varlen, plus a workspace as for fa2_bwd_ws (S * 2 * H_kv * total_tokens * d * 4
+ * bytes, from fa2_bwd_varlen_workspace_bytes; S chosen as for fa2_bwd_ws with total_tokens
+ * keys per key/value head). The reduce visits each sequence's rows only, so tokens covered by
+ * no sequence stay unwritten in dk and dv, as in fa2_bwd_varlen.
+ */
+int fa2_bwd_varlen_ws(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* delta,
+                      const int* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                      int H, int H_kv, int d, int causal, float scale, void* workspace,
+                      long long workspace_bytes, void* stream);
+long long fa2_bwd_varlen_workspace_bytes(int num_seqs, int max_seqlen, int total_tokens, int H,
+                                         int H_kv, int d, int causal);
+
 /* Number of kernel variants for head dimension d (0 if d is unsupported; a padded d has
  * the variants of its padded width). Host only. */
 int fa2_num_variants(int d);

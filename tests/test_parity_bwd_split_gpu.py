@@ -158,3 +158,43 @@ def test_ws_entry_point_checks():
     torch.cuda.synchronize()
     for x, y in zip((dq, dk, dv), ref):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_split_varlen(d):
+    """fa2_bwd_varlen_ws: packed sequences (empty, one token, tile edges) over H=8 query heads
+    and H_kv=2, plus 40 trailing tokens that no sequence covers: their dK/dV rows keep the
+    value they had, the covered rows match the oracle and the unsplit call."""
+    from oracle import attention_backward_varlen
+    from synthetic import make_varlen
+    H, H_kv, extra = 8, 2, 40
+    q, k, v, cu, lengths = make_varlen(H, d, seed=550 + d, lengths=[1, 127, 0, 128, 129, 300, 64, 2], H_kv=H_kv)
+    T0 = q.shape[1]
+    pad = lambda t: torch.cat([t, torch.ones(t.shape[0], extra, d, dtype=t.dtype)], dim=1)
+    q, k, v = pad(q), pad(k), pad(v)
+    do = _dout(q.shape, 650 + d)
+    scale = 1.0 / np.sqrt(d)
+    lib = fa2.load_library()
+    qd, kd, vd, dod, cud = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), cu.to(DEV)
+    for causal in (False, True):
+        need = lib.fa2_bwd_varlen_workspace_bytes(len(lengths), max(lengths), T0 + extra, H, H_kv, d, int(causal))
+        assert need > 0, "shape does not exercise the split"
+        tag = f"bwd split varlen d{d} causal={causal}"
+        print(f"[case] {tag}", flush=True)
+        o, lse = fa2.fwd_varlen_gqa(qd, kd, vd, cud, max(lengths), causal=causal, scale=scale)
+        rq, rk, rv = attention_backward_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                               do.double().numpy(), cu.numpy(), causal, scale)
+        outs = []
+        for split in (True, False):
+            dk = torch.full_like(kd, 7.0)
+            dv = torch.full_like(vd, 7.0)
+            dq, dk, dv = fa2.bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lengths), causal=causal, scale=scale,
+                                        dk=dk, dv=dv, split=split)
+            torch.cuda.synchronize()
+            assert torch.all(dk[:, T0:] == 7.0) and torch.all(dv[:, T0:] == 7.0), tag + ": uncovered rows written"
+            t = tag + (" ws" if split else " plain")
+            _check_grad(_f64(dq[:, :T0]), rq[:, :T0], t + " dQ")
+            _check_grad(_f64(dk[:, :T0]), rk[:, :T0], t + " dK")
+            _check_grad(_f64(dv[:, :T0]), rv[:, :T0], t + " dV")
+            outs.append((dq, dk, dv))
+        assert torch.equal(outs[0][0][:, :T0], outs[1][0][:, :T0])     # dQ is never split (uncovered rows unset)
